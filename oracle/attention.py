@@ -1,0 +1,84 @@
+"""fp64 per-segment non-causal attention (oracle; test infrastructure only).
+
+Follows ``VisionAttentionV2.forward`` on the vLLM page
+``vllm.models.dots3_note.nvidia.vision_attention``: the packed ``[T, H, D]``
+tensors are split at the ``cu_seqlens`` boundaries and every segment computes
+``softmax(q_i k_i^T * scale) v_i`` on its own, per head.  The block-diagonal
+mask of ``VisionAttention.forward`` on the same page computes the same result
+(masked entries get weight exactly zero).
+
+Readings: the page's eager forms divide by ``sqrt(head_dim)``; the tokenspeed
+page ``mm_encoder_attention.py`` (``vision_attn_flashinfer_cudnn``) defaults
+the scale to ``head_size**-0.5``.  Here the scale is an explicit argument.  The
+eager forms cast the fp32 softmax to the input dtype before the PV product;
+the oracle keeps the weights in fp64 (the exact value).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_ROW_BLOCK = 1024
+
+
+def _softmax_rows(s: np.ndarray) -> np.ndarray:
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def segment_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """One segment: q, k, v ``[s, H, D]`` -> ``[s, H, D]`` (fp64).
+
+    Query rows are taken in blocks of at most 1024 so a 16384-token segment never
+    holds its full score matrix; each row's softmax still sees every key.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    s, H, D = q.shape
+    out = np.empty((s, H, v.shape[-1]), dtype=np.float64)
+    for h in range(H):
+        kh = k[:, h, :]
+        vh = v[:, h, :]
+        for r0 in range(0, s, _ROW_BLOCK):
+            qh = q[r0:r0 + _ROW_BLOCK, h, :]
+            scores = (qh @ kh.T) * scale
+            out[r0:r0 + _ROW_BLOCK, h, :] = _softmax_rows(scores) @ vh
+    return out
+
+
+def varlen_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                     cu_seqlens: np.ndarray, scale: float) -> np.ndarray:
+    """All segments of a packed batch; rows outside ``[0, cu[N])`` are NaN."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    q = np.asarray(q, dtype=np.float64)
+    out = np.full(q.shape[:2] + (np.asarray(v).shape[-1],), np.nan, dtype=np.float64)
+    for i in range(len(cu) - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b > a:
+            out[a:b] = segment_attention(q[a:b], k[a:b], v[a:b], scale)
+    return out
+
+
+def varlen_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                          cu_seqlens: np.ndarray, scale: float,
+                          tokens: np.ndarray, heads: np.ndarray) -> np.ndarray:
+    """Selected output rows ``(tokens[j], heads[j])`` -> ``[n, D]`` (fp64).
+
+    Each row is computed on its own from its segment's keys and values, which is
+    how full-size workloads are checked one sampled row at a time.
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    heads = np.asarray(heads, dtype=np.int64)
+    seg = np.searchsorted(cu, tokens, side="right") - 1
+    out = np.empty((tokens.shape[0], np.asarray(v).shape[-1]), dtype=np.float64)
+    for j in range(tokens.shape[0]):
+        a, b = int(cu[seg[j]]), int(cu[seg[j] + 1])
+        h = int(heads[j])
+        qrow = np.asarray(q[tokens[j], h, :], dtype=np.float64)
+        kh = np.asarray(k[a:b, h, :], dtype=np.float64)
+        vh = np.asarray(v[a:b, h, :], dtype=np.float64)
+        w = _softmax_rows((kh @ qrow)[None, :] * scale)[0]
+        out[j] = w @ vh
+    return out

@@ -1,0 +1,182 @@
+/*
+ * vit.h -- C ABI of libvit.so: packed varlen (block-diagonal) multi-head
+ * attention for vision encoder towers on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  Tokens of many images are packed into one [T, H, D] tensor;
+ * int32 cu_seqlens[N+1] marks the boundaries (segment i owns tokens
+ * [cu_seqlens[i], cu_seqlens[i+1])) and every segment attends only to itself,
+ * non-causally, with no KV cache.  This is what the eager dense-mask and
+ * per-segment forms (vLLM page vllm.models.dots3_note.nvidia.vision_attention,
+ * VisionAttention.forward and VisionAttentionV2.forward) and the varlen backends
+ * (tokenspeed page mm_encoder_attention.py, vision_attn_triton / vision_attn_fa3 /
+ * vision_attn_fa4, which pass the same cu_seqlens for queries and keys) compute.
+ * A pre-pass applies the Q/K RMSNorm and the 2D rotary embedding in place.
+ *
+ * Conventions shared by every entry point:
+ *  - Status: every int-returning call returns VIT_OK (0) or a VIT_ERR_* code;
+ *    on error vit_last_error() returns a message (thread-local, valid until the
+ *    next call on the same thread).  Argument errors are detected on the host
+ *    before anything is enqueued.
+ *  - Memory: every pointer argument is device memory owned by the caller unless
+ *    stated otherwise; the library never frees or retains caller pointers.
+ *    Tensor pointers must be 16-byte aligned.
+ *  - Layout: q, k, v, out are contiguous [T, H, D] row-major, element (t, h, d)
+ *    at (t*H + h)*D + d.
+ *  - Streams: work is enqueued asynchronously on `stream` (0 = the default
+ *    stream of the current device); the library never synchronises, except
+ *    vit_device_error() and growing the scratch of vit_varlen_attn*.
+ *  - Device-side validation of cu_seqlens (see vit_varlen_worklist) never
+ *    reads or writes outside the segments it accepts.
+ *  - The caller guarantees that q, k, v and out hold at least cu_seqlens[N]
+ *    rows; the library cannot check this without a device-to-host sync.
+ */
+#ifndef VIT_H_
+#define VIT_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum vit_status {
+  VIT_OK = 0,
+  VIT_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, non-finite value */
+  VIT_ERR_UNSUPPORTED = 2, /* head dim or size outside the supported set */
+  VIT_ERR_HIP = 3          /* a HIP runtime call failed; the message names it */
+};
+
+enum vit_dtype {
+  VIT_F32 = 0,  /* IEEE binary32 */
+  VIT_BF16 = 1  /* bfloat16 (8-bit exponent, 7-bit fraction) */
+};
+
+/* Device-side error bits of one work-list build (vit_varlen_worklist), OR-ed. */
+enum vit_worklist_error {
+  VIT_WL_ERR_CU0 = 1,      /* cu_seqlens[0] != 0: the list is empty */
+  VIT_WL_ERR_NEGATIVE = 2, /* some cu_seqlens[i+1] < cu_seqlens[i]: that segment is skipped */
+  VIT_WL_ERR_TOO_LONG = 4, /* some segment longer than max_seqlen: that segment is skipped */
+  VIT_WL_ERR_CAPACITY = 8  /* more items than cap: the list is empty */
+};
+
+/*
+ * Q/K RMSNorm followed by 2D rotary embedding, in place on q and k.
+ *
+ * Norm: vLLM page vllm.models.dots3_note.nvidia.vision_attention, class
+ * _RMSNorm -- y = x * rsqrt(mean_d x^2 + eps) * w_d, the mean taken in fp32
+ * over the head dim of each (token, head) row; q uses q_weight and k uses
+ * k_weight, one [D] vector shared by all heads (_VisionAttentionBase).
+ * Rotary: VisionRotaryEmbedding on the same page gives the 1-D table
+ * inv_freq[j] = theta^(-2j/dim); here dim = D/2, so j < D/4.  Token t at grid
+ * position (row, col) gets angles a_m = row*inv_freq[m] for m < D/4 and
+ * a_m = col*inv_freq[m - D/4] for D/4 <= m < D/2, and each pair (m, m + D/2) is
+ * rotated by a_m (rotate-half with the cosine widened by concatenation, as the
+ * native rotary branch of MultimodalEncoderAttention.forward on the tokenspeed
+ * page mm_encoder_attention.py applies it).  The norm comes first, then the
+ * rotary (_qkv_with_rope).  Arithmetic is fp32; results are rounded once to the
+ * tensor dtype (nearest, ties to even).
+ *
+ *  q, k          [total_tokens, H, D] of `dtype`, updated in place.
+ *  pos           int32 [total_tokens, 2] (row, col); NULL = no rotary.
+ *  theta         rotary base, finite and > 0 (10000 in the pages).
+ *  q_weight,
+ *  k_weight      fp32 [D]; both NULL = no norm; exactly one NULL is an error.
+ *  eps           >= 0 (1e-6 in the pages).
+ *  D             a multiple of 8 in [8, 256].
+ * total_tokens == 0 is a no-op.
+ */
+int vit_qk_norm_rope(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
+                     int dtype, const int32_t* pos, float theta, const float* q_weight,
+                     const float* k_weight, float eps, hipStream_t stream);
+
+/*
+ * Varlen attention, bf16 in and out, fp32 accumulation and softmax.
+ *
+ * For every segment i, head h and query a in the segment:
+ *   out[a,h,:] = sum_b softmax_b(scale * <q[a,h,:], k[b,h,:]>) v[b,h,:],
+ * b ranging over the same segment (VisionAttentionV2.forward on the vLLM page;
+ * flash_attn_varlen_func with cu_seqlens_q = cu_seqlens_k on the tokenspeed page).
+ * The tokenspeed page defaults the scale to head_size^-0.5 when the caller
+ * passes none; here it is always explicit (any finite value).
+ *
+ *  q, k, v       bf16 [T, H, D], T = cu_seqlens[num_seqs].
+ *  cu_seqlens    int32 [num_seqs + 1] on the device.
+ *  num_seqs      N >= 0, at most 8192.
+ *  max_seqlen    an upper bound on every segment length, supplied by the
+ *                caller so no device-to-host sync is needed (the capture-safe
+ *                path of _varlen_metadata on the tokenspeed page); longer
+ *                segments are skipped and flagged (VIT_WL_ERR_TOO_LONG).
+ *  head_dim      one of 32, 64, 80, 96, 128.
+ *  out           bf16 [T, H, D]; must not alias q, k or v.  Rows of skipped
+ *                segments are left untouched.
+ * Builds the work-list in library-owned scratch (one buffer per device and
+ * stream, grown on demand with hipMalloc and kept until vit_release), then runs
+ * the attention kernel.  num_seqs == 0 or max_seqlen == 0 is a no-op.
+ */
+int vit_varlen_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                    int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
+                    void* out, hipStream_t stream);
+
+/* Same operation and parameters with fp32 q, k, v, out; fp32 arithmetic throughout. */
+int vit_varlen_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                        int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
+                        void* out, hipStream_t stream);
+
+/*
+ * Query rows per (segment, q-tile) work item of the attention kernel for this
+ * shape and dtype, or a negative VIT_ERR_* code for an unsupported shape.
+ */
+int vit_attn_block_m(int num_heads, int head_dim, int dtype);
+
+/* Work-list capacity (items) for num_seqs segments no longer than max_seqlen:
+ * num_seqs * ceil(max_seqlen / block_m); -1 on bad arguments. */
+int64_t vit_worklist_capacity(int num_seqs, int max_seqlen, int block_m);
+
+/*
+ * Work-list builder.  The pages hand cu_seqlens straight to their kernels and
+ * show no scheduler; this list is the library's own schedule:
+ *  - segment i has len_i = cu_seqlens[i+1] - cu_seqlens[i];
+ *  - segments with len_i > 0 that pass validation (enum vit_worklist_error)
+ *    are ordered by len_i descending, ties by i ascending (longest first);
+ *  - each contributes items (i, j) for j = 0 .. ceil(len_i / block_m) - 1.
+ *  items   int32 [cap, 2] (segment, q-tile), written for the first `count` rows.
+ *  cap     >= vit_worklist_capacity(num_seqs, max_seqlen, block_m).
+ *  meta    int32 [2]: meta[0] = count, meta[1] = error bits, both written.
+ * Runs entirely on the device (no host sync).  num_seqs at most 8192.
+ */
+int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int block_m,
+                        int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream);
+
+/*
+ * Attention over a work-list built by vit_varlen_worklist with
+ * block_m = vit_attn_block_m(num_heads, head_dim, dtype) for the same
+ * cu_seqlens.  Lets one list serve every layer of an encoder tower.
+ * dtype selects the bf16 (VIT_BF16) or fp32 (VIT_F32) kernel; the other
+ * arguments are those of vit_varlen_attn, and cap is the capacity the list was
+ * built with.
+ */
+int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens, const int32_t* items, int64_t cap,
+                            const int32_t* meta, int num_heads, int head_dim, float scale,
+                            int dtype, void* out, hipStream_t stream);
+
+/*
+ * Reads (and with reset != 0 clears) the work-list error bits (enum
+ * vit_worklist_error) left by the most recent vit_varlen_attn* call on the
+ * current device and `stream`.  Synchronises that stream.  *err = 0 if no such
+ * call has run yet.
+ */
+int vit_device_error(hipStream_t stream, int32_t* err, int reset);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* vit_last_error(void);
+
+/* Frees all library-owned scratch on every device (synchronises each device first). */
+void vit_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VIT_H_ */

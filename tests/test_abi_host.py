@@ -1,0 +1,135 @@
+"""Host-side checks of libvit.so that need no GPU.
+
+* the library loads and exports every function include/vit.h declares, and the
+  binding's signature table covers exactly those;
+* argument validation rejects bad calls with the documented status before any
+  HIP runtime call (null pointers are never dereferenced);
+* pure host queries (block size, work-list capacity) return the documented values.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from vision_encoder_varlen_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vit.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(vit_[a-z0-9_]+)\s*\(", text,
+                       flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("vit_qk_norm_rope", "vit_varlen_attn", "vit_varlen_attn_f32",
+                     "vit_varlen_worklist", "vit_varlen_attn_planned", "vit_attn_block_m",
+                     "vit_worklist_capacity", "vit_device_error", "vit_last_error", "vit_release"):
+        assert required in names
+    assert sorted(_lib.SIGNATURES) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_block_m_and_capacity(lib):
+    assert lib.vit_attn_block_m(16, 80, _lib.VIT_BF16) == 128
+    assert lib.vit_attn_block_m(2, 32, _lib.VIT_F32) == 32
+    assert lib.vit_attn_block_m(16, 72, _lib.VIT_BF16) == -_lib.VIT_ERR_UNSUPPORTED
+    assert lib.vit_attn_block_m(0, 64, _lib.VIT_BF16) == -_lib.VIT_ERR_INVALID_ARG
+    assert lib.vit_worklist_capacity(24, 3100, 128) == 24 * 25
+    assert lib.vit_worklist_capacity(2048, 64, 128) == 2048
+    assert lib.vit_worklist_capacity(3, 0, 64) == 0
+    assert lib.vit_worklist_capacity(-1, 5, 64) == -1
+
+
+def _err(lib):
+    return lib.vit_last_error().decode()
+
+
+FAKE = 0x10000  # aligned non-null address; never dereferenced because validation fails first
+
+
+@pytest.mark.parametrize("args,code,needle", [
+    ((None, FAKE, FAKE, FAKE, 1, 8, 2, 64, 0.125, FAKE + 0x100, None), 1, "null"),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 72, 0.125, FAKE + 0x100, None), 2, "head_dim"),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 0, 64, 0.125, FAKE + 0x100, None), 1, "num_heads"),
+    ((FAKE, FAKE, FAKE, FAKE, -1, 8, 2, 64, 0.125, FAKE + 0x100, None), 1, "num_seqs"),
+    ((FAKE, FAKE, FAKE, FAKE, 9000, 8, 2, 64, 0.125, FAKE + 0x100, None), 2, "num_seqs"),
+    ((FAKE, FAKE, FAKE, FAKE, 1, -3, 2, 64, 0.125, FAKE + 0x100, None), 1, "max_seqlen"),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 64, float("nan"), FAKE + 0x100, None), 1, "scale"),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 64, float("inf"), FAKE + 0x100, None), 1, "scale"),
+    ((FAKE + 2, FAKE, FAKE, FAKE, 1, 8, 2, 64, 0.125, FAKE + 0x100, None), 1, "aligned"),
+    ((FAKE, FAKE, FAKE, FAKE + 1, 1, 8, 2, 64, 0.125, FAKE + 0x100, None), 1, "aligned"),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 64, 0.125, FAKE, None), 1, "alias"),
+])
+def test_attention_argument_errors(lib, args, code, needle):
+    for fn in (lib.vit_varlen_attn, lib.vit_varlen_attn_f32):
+        assert fn(*args) == code
+        assert needle in _err(lib)
+
+
+def test_prepass_argument_errors(lib):
+    f = lib.vit_qk_norm_rope
+    assert f(None, FAKE, 4, 2, 64, 1, FAKE, 10000.0, None, None, 1e-6, None) == 1
+    assert f(FAKE, FAKE + 0x100, 4, 2, 60, 1, FAKE, 10000.0, None, None, 1e-6, None) == 2
+    assert f(FAKE, FAKE + 0x100, 4, 2, 64, 7, FAKE, 10000.0, None, None, 1e-6, None) == 1
+    assert f(FAKE, FAKE + 0x100, 4, 2, 64, 1, FAKE, 10000.0, FAKE, None, 1e-6, None) == 1
+    assert "both" in _err(lib)
+    assert f(FAKE, FAKE + 0x100, 4, 2, 64, 1, FAKE, -1.0, None, None, 1e-6, None) == 1
+    assert "theta" in _err(lib)
+    assert f(FAKE, FAKE + 0x100, 4, 2, 64, 1, None, 0.0, FAKE, FAKE, -1.0, None) == 1
+    assert "eps" in _err(lib)
+    assert f(FAKE, FAKE, 4, 2, 64, 1, FAKE, 10000.0, None, None, 1e-6, None) == 1
+    assert f(FAKE, FAKE + 0x100, -4, 2, 64, 1, FAKE, 10000.0, None, None, 1e-6, None) == 1
+    # nothing to do: no positions and no weights, or no tokens -> OK without touching memory
+    assert f(FAKE, FAKE + 0x100, 4, 2, 64, 1, None, 10000.0, None, None, 1e-6, None) == 0
+    assert f(FAKE, FAKE + 0x100, 0, 2, 64, 1, FAKE, 10000.0, None, None, 1e-6, None) == 0
+
+
+def test_worklist_argument_errors(lib):
+    f = lib.vit_varlen_worklist
+    meta = FAKE + 0x40
+    assert f(None, 3, 10, 64, FAKE, 3, meta, None) == 1
+    assert f(FAKE, 3, 10, 0, FAKE, 3, meta, None) == 1
+    assert f(FAKE, 3, 200, 64, FAKE, 3, meta, None) == 1      # needs 3 * 4 = 12 items
+    assert "capacity" in _err(lib)
+    assert f(FAKE, 9000, 10, 64, FAKE, 9000, meta, None) == 2
+
+
+def test_planned_argument_errors(lib):
+    f = lib.vit_varlen_attn_planned
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 5, FAKE + 0x100, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None) == 1
+    # an empty plan is a no-op
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None) == 0
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert lib.vit_varlen_attn(FAKE, FAKE, FAKE, FAKE, 0, 0, 2, 64, 0.1, FAKE + 0x100, None) == 0
+    assert lib.vit_varlen_attn(FAKE, FAKE, FAKE, FAKE, 5, 0, 2, 64, 0.1, FAKE + 0x100, None) == 0
+    assert _err(lib) == ""
+
+
+def test_error_message_is_thread_local(lib):
+    import threading
+    assert lib.vit_varlen_attn(None, FAKE, FAKE, FAKE, 1, 8, 2, 64, 0.1, FAKE + 0x100, None) == 1
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(_err(lib)))
+    t.start()
+    t.join()
+    assert seen == [""] and "null" in _err(lib)

@@ -1,0 +1,181 @@
+"""Attention kernels (bf16 MFMA and fp32) vs the fp64 oracle, plus edge cases
+and invariants, all through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+from vision_encoder_varlen_amd import workloads as W
+from gpu_util import assert_attn_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 7, 64, 65, 127, 128, 129, 300, 700]
+
+
+def _inputs(lens, H, D, dtype, seed):
+    wl = W.from_seqlens(lens, H=H, D=D, dtype=dtype, seed=seed)
+    return wl, W.generate(wl)
+
+
+def _gpu_attn(x, wl, scale=None, max_seqlen=None, guard_rows=0, out_fill=None):
+    import torch
+    from vision_encoder_varlen_amd import ops
+    T = wl.total_tokens
+    pad = np.zeros((guard_rows, wl.H, wl.D), dtype=np.float32)
+    q = to_dev(np.concatenate([x.q, pad]), wl.dtype)
+    k = to_dev(np.concatenate([x.k, pad]), wl.dtype)
+    v = to_dev(np.concatenate([x.v, pad]), wl.dtype)
+    cu = torch.from_numpy(x.cu_seqlens).cuda()
+    out = torch.full_like(q, float("nan") if out_fill is None else out_fill)
+    ops.varlen_attn(q, k, v, cu, wl.max_seqlen if max_seqlen is None else max_seqlen,
+                    wl.softmax_scale if scale is None else scale, out=out)
+    torch.cuda.synchronize()
+    got = to_host(out)
+    return got[:T], got[T:]
+
+
+@pytest.mark.parametrize("D", [32, 64, 80, 96, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_layout_matches_oracle(D, dtype):
+    wl, x = _inputs(RAGGED, H=3, D=D, dtype=dtype, seed=D)
+    got, _ = _gpu_attn(x, wl)
+    want = oracle.varlen_attention(x.q, x.k, x.v, x.cu_seqlens, wl.softmax_scale)
+    assert_attn_close(got, want, dtype, f"D={D} {dtype}")
+
+
+@pytest.mark.parametrize("H", [1, 12, 16])
+def test_head_counts(H):
+    wl, x = _inputs([200, 33, 513], H=H, D=64, dtype="bf16", seed=H)
+    got, _ = _gpu_attn(x, wl)
+    want = oracle.varlen_attention(x.q, x.k, x.v, x.cu_seqlens, wl.softmax_scale)
+    assert_attn_close(got, want, "bf16", f"H={H}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_empty_segments_and_guard_rows(dtype):
+    lens = [0, 5, 0, 0, 130, 0, 1]
+    wl, x = _inputs(lens, H=2, D=64, dtype=dtype, seed=3)
+    got, guard = _gpu_attn(x, wl, guard_rows=16, out_fill=7.0)
+    want = oracle.varlen_attention(x.q, x.k, x.v, x.cu_seqlens, wl.softmax_scale)
+    assert_attn_close(got, want, dtype, "empty segments")
+    assert np.all(guard == 7.0), "rows beyond cu_seqlens[N] were written"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_length_one_segment_returns_its_value_row_bit_exact(dtype):
+    wl, x = _inputs([1, 40, 1, 1, 200, 1], H=4, D=128, dtype=dtype, seed=4)
+    got, _ = _gpu_attn(x, wl)
+    for t in (0, 41, 42, 243):
+        assert np.array_equal(got[t], x.v[t].astype(np.float64)), t
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_constant_values_return_the_constant(dtype):
+    wl, x = _inputs([77, 300], H=2, D=80, dtype=dtype, seed=5)
+    v = x.v.copy()
+    v[:77] = v[0]
+    v[77:] = v[77]
+    x.v = v
+    got, _ = _gpu_attn(x, wl)
+    tol = 1e-5 if dtype == "f32" else 2.0 ** -7 * np.abs(v).max()
+    assert np.max(np.abs(got - v)) <= tol
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_scale_gives_segment_mean(dtype):
+    wl, x = _inputs([50, 130], H=2, D=64, dtype=dtype, seed=6)
+    got, _ = _gpu_attn(x, wl, scale=0.0)
+    want = oracle.varlen_attention(x.q, x.k, x.v, x.cu_seqlens, 0.0)
+    assert_attn_close(got, want, dtype, "scale 0")
+
+
+def test_large_scores_stay_stable():
+    wl, x = _inputs([90, 257], H=2, D=128, dtype="bf16", seed=7)
+    x.q = x.q * 8.0   # exact in bf16; logits of order 100
+    got, _ = _gpu_attn(x, wl)
+    want = oracle.varlen_attention(x.q, x.k, x.v, x.cu_seqlens, wl.softmax_scale)
+    assert_attn_close(got, want, "bf16", "peaked softmax")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_segment_isolation_is_bit_exact(dtype):
+    lens = [100, 260, 31]
+    wl, x = _inputs(lens, H=2, D=64, dtype=dtype, seed=8)
+    a, _ = _gpu_attn(x, wl)
+    for arr in (x.q, x.k, x.v):
+        arr[100:360] = arr[100:360] * -0.5
+    b, _ = _gpu_attn(x, wl)
+    assert np.array_equal(a[:100], b[:100]) and np.array_equal(a[360:], b[360:])
+    assert not np.allclose(a[100:360], b[100:360])
+
+
+def test_segment_permutation_permutes_outputs():
+    lens = [100, 260, 31]
+    wl, x = _inputs(lens, H=2, D=64, dtype="bf16", seed=9)
+    a, _ = _gpu_attn(x, wl)
+    cu = x.cu_seqlens
+    order = [2, 0, 1]
+    idx = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in order])
+    wl2 = W.from_seqlens([lens[i] for i in order], H=2, D=64, dtype="bf16")
+    x2 = W.Inputs(q=x.q[idx], k=x.k[idx], v=x.v[idx], wq=x.wq, wk=x.wk, pos=x.pos[idx],
+                  cu_seqlens=wl2.cu_seqlens)
+    b, _ = _gpu_attn(x2, wl2)
+    assert np.array_equal(b, a[idx])
+
+
+def test_results_are_deterministic():
+    wl, x = _inputs(RAGGED, H=3, D=80, dtype="bf16", seed=10)
+    a, _ = _gpu_attn(x, wl)
+    b, _ = _gpu_attn(x, wl)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_planned_path_equals_direct_path(dtype):
+    import torch
+    from vision_encoder_varlen_amd import ops
+    wl, x = _inputs(RAGGED, H=2, D=128, dtype=dtype, seed=11)
+    direct, _ = _gpu_attn(x, wl)
+    q, k, v = (to_dev(a, dtype) for a in (x.q, x.k, x.v))
+    cu = torch.from_numpy(x.cu_seqlens).cuda()
+    plan = ops.varlen_worklist(cu, wl.max_seqlen, ops.attn_block_m(2, 128, q.dtype))
+    outs = [ops.varlen_attn_planned(q, k, v, cu, plan, wl.softmax_scale) for _ in range(2)]
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(to_host(o), direct)
+
+
+def test_understated_max_seqlen_skips_and_flags():
+    import torch
+    from vision_encoder_varlen_amd import ops
+    wl, x = _inputs([40, 300, 90], H=2, D=64, dtype="bf16", seed=12)
+    ops.device_error(reset=True)
+    got, _ = _gpu_attn(x, wl, max_seqlen=128, out_fill=3.0)
+    assert ops.device_error() == 4
+    assert np.all(got[40:340] == 3.0)
+    want = oracle.varlen_attention(x.q, x.k, x.v, x.cu_seqlens, wl.softmax_scale)
+    assert_attn_close(got[:40], want[:40], "bf16", "first segment")
+    assert_attn_close(got[340:], want[340:], "bf16", "last segment")
+    _gpu_attn(x, wl)
+    assert ops.device_error() == 0
+    torch.cuda.synchronize()
+
+
+def test_no_segments_is_a_no_op():
+    import torch
+    from vision_encoder_varlen_amd import ops
+    q = torch.zeros((4, 2, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.full_like(q, 5.0)
+    ops.varlen_attn(q, q.clone(), q.clone(), torch.zeros(1, dtype=torch.int32, device="cuda"), 0,
+                    out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 5.0)
+
+
+def test_errors_raise_value_error():
+    import torch
+    from vision_encoder_varlen_amd import ops
+    q = torch.zeros((4, 2, 72), dtype=torch.bfloat16, device="cuda")
+    cu = torch.tensor([0, 4], dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="head_dim"):
+        ops.varlen_attn(q, q.clone(), q.clone(), cu, 4)

@@ -1,0 +1,141 @@
+// Varlen (block-diagonal) non-causal attention in fp32 throughout.
+//
+// Same operation as attn_bf16.hip (vLLM page
+// vllm.models.dots3_note.nvidia.vision_attention, VisionAttentionV2.forward),
+// for fp32 tensors where an exact-precision result is wanted.  No MFMA and no
+// down-conversion: products and sums are fp32 FMAs and the softmax uses the
+// accurate expf.
+//
+// One workgroup = one wave = 32 query rows of one head.  Lanes l and l+32 share
+// query row l: each holds half of the head dim of q and of the output
+// accumulator, and the two partial dot products are joined with one lane
+// exchange, so both lanes see bit-identical scores.  Keys stream through LDS in
+// tiles of 32 rows with a per-key online softmax.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "vit_kernels.h"
+
+namespace vit {
+namespace {
+
+constexpr int kBM = kBlockMF32;
+constexpr int kBN = 32;
+constexpr int kThreads = 64;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
+    const int32_t* __restrict__ meta, int H, float scale, float* __restrict__ out) {
+  constexpr int HD = D / 2;
+  constexpr int ROW = D + 4;  // +16 bytes per LDS row
+  __shared__ __align__(16) float ks[kBN * ROW];
+  __shared__ __align__(16) float vs[kBN * ROW];
+
+  const int lane = threadIdx.x;
+  const int r = lane & 31;
+  const int half = lane >> 5;
+  const size_t tok_stride = size_t(H) * D;
+
+  const int64_t nunits = int64_t(meta[0]) * H;
+  for (int64_t unit = blockIdx.x; unit < nunits; unit += gridDim.x) {
+    const int item = int(unit / H);
+    const int h = int(unit - int64_t(item) * H);
+    const int seg = items[2 * item];
+    const int qt = items[2 * item + 1];
+    const int start = cu[seg];
+    const int len = cu[seg + 1] - start;
+    const int qrow = qt * kBM + r;
+
+    float qv[HD], acc[HD];
+#pragma unroll
+    for (int d = 0; d < HD; ++d) acc[d] = 0.f;
+    if (qrow < len) {
+      const float* qp = q + size_t(start + qrow) * tok_stride + size_t(h) * D + half * HD;
+#pragma unroll
+      for (int d = 0; d < HD; d += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(qp + d);
+        qv[d] = x.x; qv[d + 1] = x.y; qv[d + 2] = x.z; qv[d + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < HD; ++d) qv[d] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+
+    for (int kv0 = 0; kv0 < len; kv0 += kBN) {
+      __syncthreads();  // previous tile fully consumed
+      for (int c = lane; c < kBN * (D / 4); c += kThreads) {
+        const int key = c / (D / 4);
+        const int dc = c - key * (D / 4);
+        float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+        if (kv0 + key < len) {
+          const size_t off = size_t(start + kv0 + key) * tok_stride + size_t(h) * D + dc * 4;
+          kx = *reinterpret_cast<const float4*>(k + off);
+          vx = *reinterpret_cast<const float4*>(v + off);
+        }
+        *reinterpret_cast<float4*>(ks + key * ROW + dc * 4) = kx;
+        *reinterpret_cast<float4*>(vs + key * ROW + dc * 4) = vx;
+      }
+      __syncthreads();
+      const int nk = len - kv0 < kBN ? len - kv0 : kBN;
+      for (int j = 0; j < nk; ++j) {
+        const float* kr = ks + j * ROW + half * HD;
+        float part = 0.f;
+#pragma unroll
+        for (int d = 0; d < HD; ++d) part = fmaf(qv[d], kr[d], part);
+        const float sc = (part + __shfl_xor(part, 32)) * scale;
+        const float m_new = fmaxf(m, sc);
+        const float alpha = expf(m - m_new);
+        const float p = expf(sc - m_new);
+        m = m_new;
+        l = l * alpha + p;
+        const float* vr = vs + j * ROW + half * HD;
+#pragma unroll
+        for (int d = 0; d < HD; ++d) acc[d] = fmaf(p, vr[d], acc[d] * alpha);
+      }
+    }
+
+    if (qrow < len) {
+      const float inv = 1.f / l;
+      float* op = out + size_t(start + qrow) * tok_stride + size_t(h) * D + half * HD;
+#pragma unroll
+      for (int d = 0; d < HD; d += 4)
+        *reinterpret_cast<float4*>(op + d) =
+            make_float4(acc[d] * inv, acc[d + 1] * inv, acc[d + 2] * inv, acc[d + 3] * inv);
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* cu,
+                    const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
+                    void* out, hipStream_t stream) {
+  const int64_t units = cap * int64_t(H);
+  if (units <= 0) return hipSuccess;
+  const int64_t grid = units < kMaxAttnGrid ? units : kMaxAttnGrid;
+  hipLaunchKernelGGL(attn_f32_kernel<D>, dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+                     static_cast<const float*>(q), static_cast<const float*>(k),
+                     static_cast<const float*>(v), cu, items, meta, H, scale,
+                     static_cast<float*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu,
+                           const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
+                           float scale, void* out, hipStream_t stream) {
+  switch (D) {
+    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
+    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
+    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
+    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
+    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace vit

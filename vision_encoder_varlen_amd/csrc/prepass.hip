@@ -1,0 +1,202 @@
+// Fused Q/K RMSNorm + 2D rotary embedding, in place, fp32 arithmetic.
+//
+// Norm: vLLM page vllm.models.dots3_note.nvidia.vision_attention, _RMSNorm
+// (mean of squares over the head dim, fp32 reduce, rsqrt, times a [D] weight
+// shared by all heads).  Rotary: VisionRotaryEmbedding on the same page, with
+// the row index looking up the first D/4 frequencies and the column index the
+// next D/4, applied rotate-half to pairs (m, m + D/2) -- the native rotary
+// branch of MultimodalEncoderAttention.forward on the tokenspeed page
+// mm_encoder_attention.py widens a half-width cosine the same way.  Order: norm,
+// then rotary (_qkv_with_rope).
+//
+// Memory-bound.  A workgroup takes a group of tokens:
+//  1. cos/sin of the token group's D/2 angles go to LDS, so each angle is
+//     evaluated once per token rather than once per head and tensor (accurate
+//     sincosf; the inverse frequencies arrive precomputed in the kernel
+//     arguments);
+//  2. each (token, head) row is handled by G = next_pow2(D/8) consecutive lanes;
+//     a lane owns dims m..m+3 and their rotary partners m+D/2..m+D/2+3, so the
+//     rotation is lane-local and only the sum of squares crosses lanes (a
+//     log2(G)-step xor shuffle inside the lane group).  Loads and stores are 8
+//     bytes (bf16) or 16 bytes (fp32) per lane per half row, and every row is
+//     read and written exactly once.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "vit_kernels.h"
+
+namespace vit {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxD = 256;
+
+// Inverse frequencies as unevaluated sums hi + lo of two floats (about 48
+// significant bits), so the angle pos * inv_freq can be formed to fp32
+// accuracy at any position.
+struct Freqs {
+  float hi[kMaxD / 4];
+  float lo[kMaxD / 4];
+};
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16;
+
+__device__ __forceinline__ float bf16_to_f32(unsigned int bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ void load4(const float* p, float x[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+__device__ __forceinline__ void store4(float* p, const float x[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void load4(const u16* p, float x[4]) {
+  const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
+  x[0] = bf16_to_f32(v.x & 0xffffu); x[1] = bf16_to_f32(v.x >> 16);
+  x[2] = bf16_to_f32(v.y & 0xffffu); x[3] = bf16_to_f32(v.y >> 16);
+}
+__device__ __forceinline__ void store4(u16* p, const float x[4]) {
+  __bf16 w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = (__bf16)x[e];  // round to nearest even
+  *reinterpret_cast<u32x2_t*>(p) = __builtin_bit_cast(u32x2_t, w);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void prepass_kernel(
+    T* __restrict__ q, T* __restrict__ k, long long T_tok, int H, int D, int G, int tok_per_grp,
+    const int32_t* __restrict__ pos, Freqs freqs, const float* __restrict__ wq,
+    const float* __restrict__ wk, float eps) {
+  extern __shared__ float2 cs[];  // [tok_per_grp][D/2] (cos, sin)
+  const int tid = threadIdx.x;
+  const int half_d = D / 2;
+  const int quarter_d = D / 4;
+  const bool rope = pos != nullptr;
+  const bool norm = wq != nullptr;
+  const float inv_d = 1.f / float(D);
+
+  const int lane_g = tid & (G - 1);        // lane inside the row group
+  const int m0 = lane_g * 4;                // first dim of this lane (first half)
+  const bool lane_active = m0 < half_d;
+  const int rows_per_pass = kThreads / G;
+  const int rows_per_grp = tok_per_grp * H;
+
+  for (long long t0 = (long long)blockIdx.x * tok_per_grp; t0 < T_tok;
+       t0 += (long long)gridDim.x * tok_per_grp) {
+    const int ntok = T_tok - t0 < tok_per_grp ? int(T_tok - t0) : tok_per_grp;
+    if (rope) {
+      for (int i = tid; i < ntok * half_d; i += kThreads) {
+        const int tl = i / half_d;
+        const int m = i - tl * half_d;
+        const long long t = t0 + tl;
+        const float coord = m < quarter_d ? float(pos[2 * t]) : float(pos[2 * t + 1]);
+        const int j = m < quarter_d ? m : m - quarter_d;
+        // angle = a_hi + a_lo exactly up to the rounding of a_lo: fmaf recovers
+        // the rounding error of coord * hi.
+        const float a_hi = coord * freqs.hi[j];
+        const float a_lo = fmaf(coord, freqs.hi[j], -a_hi) + coord * freqs.lo[j];
+        float s, c;
+        sincosf(a_hi, &s, &c);
+        // first-order correction for a_lo (|a_lo| <= 2^-23 |a_hi|; the neglected
+        // second-order term is below 2^-46 |a_hi|^2)
+        cs[i] = make_float2(fmaf(-s, a_lo, c), fmaf(c, a_lo, s));
+      }
+      __syncthreads();
+    }
+
+    for (int r0 = 0; r0 < ntok * H; r0 += rows_per_pass) {
+      const int row = r0 + tid / G;  // (token_local, head) row inside the group
+      const bool row_ok = row < ntok * H && lane_active;
+      const int tl = row / H;
+      const int h = row - tl * H;
+      const size_t base = (size_t(t0 + tl) * H + h) * size_t(D);
+#pragma unroll
+      for (int which = 0; which < 2; ++which) {
+        T* const x_ptr = which == 0 ? q : k;
+        const float* const w = which == 0 ? wq : wk;
+        float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+        if (row_ok) {
+          load4(x_ptr + base + m0, a);
+          load4(x_ptr + base + m0 + half_d, b);
+        }
+        if (norm) {
+          float ss = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss = fmaf(a[e], a[e], fmaf(b[e], b[e], ss));
+          for (int off = G >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+          const float rinv = rsqrtf(ss * inv_d + eps);
+          if (row_ok) {
+            float wa[4], wb[4];
+            load4(w + m0, wa);
+            load4(w + m0 + half_d, wb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              a[e] = a[e] * rinv * wa[e];
+              b[e] = b[e] * rinv * wb[e];
+            }
+          }
+        }
+        if (rope && row_ok) {
+          const float2* c = cs + tl * half_d + m0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float2 cse = c[e];
+            const float ya = a[e] * cse.x - b[e] * cse.y;
+            const float yb = b[e] * cse.x + a[e] * cse.y;
+            a[e] = ya;
+            b[e] = yb;
+          }
+        }
+        if (row_ok) {
+          store4(x_ptr + base + m0, a);
+          store4(x_ptr + base + m0 + half_d, b);
+        }
+      }
+    }
+    (void)rows_per_grp;
+    if (rope) __syncthreads();  // cs is rewritten by the next token group
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
+                          const int32_t* pos, const double* inv_freq_host, const float* wq,
+                          const float* wk, float eps, hipStream_t stream) {
+  if (T <= 0 || (pos == nullptr && wq == nullptr)) return hipSuccess;
+  int G = 1;
+  while (G * 8 < D) G <<= 1;                 // lanes per (token, head) row
+  const int rows_per_pass = kThreads / G;
+  // About eight rows per lane per token group keeps loads in flight while the
+  // cos/sin table stays small.
+  int tok_per_grp = (8 * rows_per_pass) / H;
+  if (tok_per_grp < 1) tok_per_grp = 1;
+  const int max_tok_lds = 32768 / (D / 2 * int(sizeof(float) * 2));
+  if (tok_per_grp > max_tok_lds) tok_per_grp = max_tok_lds;
+  Freqs fr{};
+  if (pos != nullptr) {
+    for (int j = 0; j < D / 4; ++j) {
+      fr.hi[j] = float(inv_freq_host[j]);
+      fr.lo[j] = float(inv_freq_host[j] - double(fr.hi[j]));
+    }
+  }
+  const long long groups = (T + tok_per_grp - 1) / tok_per_grp;
+  const long long grid = groups < 65536 ? groups : 65536;
+  const size_t lds = pos != nullptr ? size_t(tok_per_grp) * (D / 2) * sizeof(float) * 2 : 0;
+  if (dtype == 1) {
+    hipLaunchKernelGGL(prepass_kernel<u16>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
+                       static_cast<u16*>(q), static_cast<u16*>(k), (long long)T, H, D, G,
+                       tok_per_grp, pos, fr, wq, wk, eps);
+  } else {
+    hipLaunchKernelGGL(prepass_kernel<float>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
+                       static_cast<float*>(q), static_cast<float*>(k), (long long)T, H, D, G,
+                       tok_per_grp, pos, fr, wq, wk, eps);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vit

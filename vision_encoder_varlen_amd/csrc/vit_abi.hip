@@ -1,0 +1,266 @@
+// C ABI of libvit.so (declared in include/vit.h): argument validation on the
+// host, error reporting, library-owned work-list scratch, kernel launches.
+//
+// Every argument check runs before the first HIP runtime call, so a rejected
+// call enqueues nothing and touches no device state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "vit.h"
+#include "vit_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(VIT_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+int ok() {
+  g_last_error.clear();
+  return VIT_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Work-list scratch owned by the library: one buffer per (device, stream), so
+// calls on different streams never share it.  Layout: meta[4] then items.
+struct Scratch {
+  int32_t* buf = nullptr;
+  int64_t cap_items = 0;
+};
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+
+constexpr int64_t kMaxCapacity = int64_t(1) << 30;
+
+int64_t capacity(int num_seqs, int max_seqlen, int block_m) {
+  if (num_seqs < 0 || max_seqlen < 0 || block_m <= 0) return -1;
+  return int64_t(num_seqs) * ((int64_t(max_seqlen) + block_m - 1) / block_m);
+}
+
+int get_scratch(hipStream_t stream, int64_t cap, Scratch** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  Scratch& s = g_scratch[{dev, stream}];
+  if (s.cap_items < cap) {
+    if (s.buf != nullptr) {
+      // The old buffer may still be read by work queued on this stream.
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+      e = hipFree(s.buf);
+      if (e != hipSuccess) return hip_fail(e, "hipFree");
+      s.buf = nullptr;
+      s.cap_items = 0;
+    }
+    int64_t grow = cap < 4096 ? 4096 : cap + cap / 4;
+    e = hipMalloc(reinterpret_cast<void**>(&s.buf), size_t(4 + 2 * grow) * sizeof(int32_t));
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc (work-list scratch)");
+    s.cap_items = grow;
+  }
+  *out = &s;
+  return VIT_OK;
+}
+
+int check_attn_args(const void* q, const void* k, const void* v, const int32_t* cu,
+                    int num_seqs, int max_seqlen, int H, int D, float scale, const void* out) {
+  if (!q || !k || !v || !cu || !out) return fail(VIT_ERR_INVALID_ARG, "null pointer argument");
+  if (num_seqs < 0) return fail(VIT_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (num_seqs > vit::kWorklistMaxSeqs)
+    return fail(VIT_ERR_UNSUPPORTED, "num_seqs %d exceeds the supported maximum %d", num_seqs,
+                vit::kWorklistMaxSeqs);
+  if (max_seqlen < 0) return fail(VIT_ERR_INVALID_ARG, "max_seqlen must be >= 0 (got %d)", max_seqlen);
+  if (H < 1) return fail(VIT_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", H);
+  if (!vit::attn_head_dim_supported(D))
+    return fail(VIT_ERR_UNSUPPORTED, "head_dim %d not supported (supported: 32, 64, 80, 96, 128)", D);
+  if (!std::isfinite(scale)) return fail(VIT_ERR_INVALID_ARG, "scale must be finite");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(VIT_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (!aligned4(cu)) return fail(VIT_ERR_INVALID_ARG, "cu_seqlens must be 4-byte aligned");
+  if (out == q || out == k || out == v) return fail(VIT_ERR_INVALID_ARG, "out must not alias q, k or v");
+  return VIT_OK;
+}
+
+int block_m_for(int dtype) { return dtype == VIT_BF16 ? vit::kBlockMBf16 : vit::kBlockMF32; }
+
+int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, int num_seqs,
+                int max_seqlen, int H, int D, float scale, void* out, hipStream_t stream,
+                int dtype) {
+  int rc = check_attn_args(q, k, v, cu, num_seqs, max_seqlen, H, D, scale, out);
+  if (rc != VIT_OK) return rc;
+  if (num_seqs == 0 || max_seqlen == 0) return ok();
+  const int bm = block_m_for(dtype);
+  const int64_t cap = capacity(num_seqs, max_seqlen, bm);
+  if (cap > kMaxCapacity) return fail(VIT_ERR_UNSUPPORTED, "work-list capacity %lld too large", (long long)cap);
+  Scratch* s = nullptr;
+  rc = get_scratch(stream, cap, &s);
+  if (rc != VIT_OK) return rc;
+  int32_t* meta = s->buf;
+  int32_t* items = s->buf + 4;
+  hipError_t e = vit::launch_worklist(cu, num_seqs, max_seqlen, bm, items, cap, meta, stream);
+  if (e != hipSuccess) return hip_fail(e, "work-list launch");
+  e = dtype == VIT_BF16
+          ? vit::launch_attn_bf16(q, k, v, cu, items, cap, meta, H, D, scale, out, stream)
+          : vit::launch_attn_f32(q, k, v, cu, items, cap, meta, H, D, scale, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int vit_qk_norm_rope(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
+                     int dtype, const int32_t* pos, float theta, const float* q_weight,
+                     const float* k_weight, float eps, hipStream_t stream) {
+  if (!q || !k) return fail(VIT_ERR_INVALID_ARG, "null q or k");
+  if (total_tokens < 0) return fail(VIT_ERR_INVALID_ARG, "total_tokens must be >= 0");
+  if (num_heads < 1) return fail(VIT_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", num_heads);
+  if (head_dim < 8 || head_dim > 256 || head_dim % 8 != 0)
+    return fail(VIT_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 in [8, 256] (got %d)", head_dim);
+  if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if ((q_weight == nullptr) != (k_weight == nullptr))
+    return fail(VIT_ERR_INVALID_ARG, "give both q_weight and k_weight or neither");
+  if (pos != nullptr && (!std::isfinite(theta) || theta <= 0.f))
+    return fail(VIT_ERR_INVALID_ARG, "theta must be finite and > 0");
+  if (q_weight != nullptr && (!std::isfinite(eps) || eps < 0.f))
+    return fail(VIT_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!aligned16(q) || !aligned16(k)) return fail(VIT_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  if (q_weight && (!aligned16(q_weight) || !aligned16(k_weight)))
+    return fail(VIT_ERR_INVALID_ARG, "norm weights must be 16-byte aligned");
+  if (pos && !aligned4(pos)) return fail(VIT_ERR_INVALID_ARG, "pos must be 4-byte aligned");
+  if (q == k) return fail(VIT_ERR_INVALID_ARG, "q and k must be distinct buffers");
+  if (total_tokens == 0 || (pos == nullptr && q_weight == nullptr)) return ok();
+  // Rotary inverse frequencies for dim = D/2: theta^(-2j/(D/2)), in double.
+  double inv_freq[64];
+  const int F = head_dim / 4;
+  for (int j = 0; j < F; ++j) inv_freq[j] = std::pow(double(theta), -2.0 * j / (head_dim / 2.0));
+  hipError_t e = vit::launch_prepass(q, k, total_tokens, num_heads, head_dim, dtype, pos,
+                                     inv_freq, q_weight, k_weight, eps, stream);
+  if (e != hipSuccess) return hip_fail(e, "pre-pass launch");
+  return ok();
+}
+
+int vit_varlen_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                    int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
+                    void* out, hipStream_t stream) {
+  return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, out,
+                     stream, VIT_BF16);
+}
+
+int vit_varlen_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                        int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
+                        void* out, hipStream_t stream) {
+  return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, out,
+                     stream, VIT_F32);
+}
+
+int vit_attn_block_m(int num_heads, int head_dim, int dtype) {
+  if (num_heads < 1) return -fail(VIT_ERR_INVALID_ARG, "num_heads must be >= 1");
+  if (!vit::attn_head_dim_supported(head_dim))
+    return -fail(VIT_ERR_UNSUPPORTED, "head_dim %d not supported", head_dim);
+  if (dtype != VIT_F32 && dtype != VIT_BF16) return -fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  ok();
+  return block_m_for(dtype);
+}
+
+int64_t vit_worklist_capacity(int num_seqs, int max_seqlen, int block_m) {
+  return capacity(num_seqs, max_seqlen, block_m);
+}
+
+int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int block_m,
+                        int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream) {
+  if (!cu_seqlens || !items || !meta) return fail(VIT_ERR_INVALID_ARG, "null pointer argument");
+  if (num_seqs < 0 || max_seqlen < 0) return fail(VIT_ERR_INVALID_ARG, "negative size");
+  if (num_seqs > vit::kWorklistMaxSeqs)
+    return fail(VIT_ERR_UNSUPPORTED, "num_seqs %d exceeds the supported maximum %d", num_seqs,
+                vit::kWorklistMaxSeqs);
+  if (block_m <= 0) return fail(VIT_ERR_INVALID_ARG, "block_m must be > 0");
+  const int64_t need = capacity(num_seqs, max_seqlen, block_m);
+  if (need > kMaxCapacity) return fail(VIT_ERR_UNSUPPORTED, "work-list capacity %lld too large", (long long)need);
+  if (cap < need)
+    return fail(VIT_ERR_INVALID_ARG, "cap %lld below the required capacity %lld", (long long)cap,
+                (long long)need);
+  if (!aligned4(cu_seqlens) || !aligned4(items) || !aligned4(meta))
+    return fail(VIT_ERR_INVALID_ARG, "int32 buffers must be 4-byte aligned");
+  hipError_t e = vit::launch_worklist(cu_seqlens, num_seqs, max_seqlen, block_m, items, cap, meta, stream);
+  if (e != hipSuccess) return hip_fail(e, "work-list launch");
+  return ok();
+}
+
+int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens, const int32_t* items, int64_t cap,
+                            const int32_t* meta, int num_heads, int head_dim, float scale,
+                            int dtype, void* out, hipStream_t stream) {
+  if (!items || !meta) return fail(VIT_ERR_INVALID_ARG, "null work-list pointer");
+  if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  int rc = check_attn_args(q, k, v, cu_seqlens, 0, 0, num_heads, head_dim, scale, out);
+  if (rc != VIT_OK) return rc;
+  if (cap < 0 || cap > kMaxCapacity) return fail(VIT_ERR_INVALID_ARG, "bad work-list capacity %lld", (long long)cap);
+  if (cap == 0) return ok();
+  hipError_t e = dtype == VIT_BF16
+      ? vit::launch_attn_bf16(q, k, v, cu_seqlens, items, cap, meta, num_heads, head_dim, scale, out, stream)
+      : vit::launch_attn_f32(q, k, v, cu_seqlens, items, cap, meta, num_heads, head_dim, scale, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+int vit_device_error(hipStream_t stream, int32_t* err, int reset) {
+  if (!err) return fail(VIT_ERR_INVALID_ARG, "null err pointer");
+  *err = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto it = g_scratch.find({dev, stream});
+  if (it == g_scratch.end() || it->second.buf == nullptr) return ok();
+  e = hipMemcpyAsync(err, it->second.buf + 1, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "reading the work-list error word");
+  if (reset) {
+    const int32_t zero = 0;
+    e = hipMemcpyAsync(it->second.buf + 1, &zero, sizeof(int32_t), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "clearing the work-list error word");
+  }
+  return ok();
+}
+
+const char* vit_last_error(void) { return g_last_error.c_str(); }
+
+void vit_release(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (auto& kv : g_scratch) {
+    if (kv.second.buf == nullptr) continue;
+    int cur = 0;
+    if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first.first) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(kv.second.buf);
+      (void)hipSetDevice(cur);
+    }
+  }
+  g_scratch.clear();
+}
+
+}  // extern "C"

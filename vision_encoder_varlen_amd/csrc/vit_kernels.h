@@ -1,0 +1,41 @@
+// Internal launch interface between the C ABI (vit_abi.hip) and the kernels.
+// Not installed; the public interface is include/vit.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vit {
+
+// Query rows per (segment, q-tile) work item.
+constexpr int kBlockMBf16 = 128;  // 4 waves x 32 rows, bf16 MFMA kernel
+constexpr int kBlockMF32 = 32;    // 1 wave, lane pairs share a row, fp32 kernel
+
+// Work-list builder limits: one workgroup sorts every segment in LDS.
+constexpr int kWorklistMaxSeqs = 8192;
+
+// Upper bound on attention workgroups per launch; larger work loops inside.
+constexpr int64_t kMaxAttnGrid = int64_t(1) << 22;
+
+inline bool attn_head_dim_supported(int D) {
+  return D == 32 || D == 64 || D == 80 || D == 96 || D == 128;
+}
+
+// Pre-pass: inv_freq_host holds the D/4 rotary inverse frequencies in double
+// (may be null when pos is null).  dtype: 0 = fp32, 1 = bf16.
+hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
+                          const int32_t* pos, const double* inv_freq_host,
+                          const float* wq, const float* wk, float eps, hipStream_t stream);
+
+hipError_t launch_worklist(const int32_t* cu, int N, int max_seqlen, int block_m,
+                           int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream);
+
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const int32_t* cu,
+                            const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
+                            float scale, void* out, hipStream_t stream);
+
+hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu,
+                           const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
+                           float scale, void* out, hipStream_t stream);
+
+}  // namespace vit

@@ -1,0 +1,185 @@
+"""PyTorch-facing wrappers over the C ABI of libvit.so.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream.  Errors from the
+library raise ``VitError`` (a ``ValueError``) carrying its message.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.VIT_F32, torch.bfloat16: _lib.VIT_BF16}
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need_cuda(name: str, t: torch.Tensor, dtype=None) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    if dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dtype}; expected float32 or bfloat16")
+    return _DTYPES[dtype]
+
+
+def qk_norm_rope_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch.Tensor] = None,
+                  theta: float = 10000.0, q_weight: Optional[torch.Tensor] = None,
+                  k_weight: Optional[torch.Tensor] = None, eps: float = 1e-6) -> None:
+    """In-place Q/K RMSNorm (when weights are given) then 2D rotary (when ``pos`` is given)."""
+    _need_cuda("q", q)
+    _need_cuda("k", k, q.dtype)
+    if q.dim() != 3 or k.shape != q.shape:
+        raise ValueError("q and k must both be [T, H, D]")
+    T, H, D = q.shape
+    if pos is not None:
+        _need_cuda("pos", pos, torch.int32)
+        if pos.shape != (T, 2):
+            raise ValueError("pos must be int32 [T, 2]")
+    for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
+        if w is not None:
+            _need_cuda(name, w, torch.float32)
+            if w.shape != (D,):
+                raise ValueError(f"{name} must be float32 [D]")
+    _lib.check(_lib.load().vit_qk_norm_rope(
+        q.data_ptr(), k.data_ptr(), T, H, D, dtype_code(q.dtype), _ptr(pos), float(theta),
+        _ptr(q_weight), _ptr(k_weight), float(eps), _stream(q)))
+
+
+def _attn_checks(q, k, v, cu_seqlens):
+    _need_cuda("q", q)
+    for name, t in (("k", k), ("v", v)):
+        _need_cuda(name, t, q.dtype)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q")
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, D]")
+    _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be int32 [N+1]")
+
+
+def varlen_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                max_seqlen: int, scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block-diagonal non-causal attention over packed ``[T, H, D]`` tensors.
+
+    ``scale`` defaults to ``head_dim ** -0.5``.  Dispatches on dtype: bf16 uses
+    the MFMA kernel, fp32 the fp32 kernel.  Returns ``out``.
+    """
+    _attn_checks(q, k, v, cu_seqlens)
+    T, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_cuda("out", out, q.dtype)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    lib = _lib.load()
+    fn = lib.vit_varlen_attn if q.dtype == torch.bfloat16 else lib.vit_varlen_attn_f32
+    dtype_code(q.dtype)
+    _lib.check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
+                  cu_seqlens.numel() - 1, int(max_seqlen), H, D, float(scale), out.data_ptr(),
+                  _stream(q)))
+    return out
+
+
+def attn_block_m(num_heads: int, head_dim: int, dtype: torch.dtype) -> int:
+    bm = _lib.load().vit_attn_block_m(num_heads, head_dim, dtype_code(dtype))
+    if bm < 0:
+        _lib.check(-bm)
+    return bm
+
+
+def worklist_capacity(num_seqs: int, max_seqlen: int, block_m: int) -> int:
+    return int(_lib.load().vit_worklist_capacity(num_seqs, max_seqlen, block_m))
+
+
+class Plan:
+    """A device work-list for one ``cu_seqlens``, reusable across layers."""
+
+    def __init__(self, items: torch.Tensor, meta: torch.Tensor, cap: int, block_m: int,
+                 num_seqs: int, max_seqlen: int):
+        self.items, self.meta, self.cap, self.block_m = items, meta, cap, block_m
+        self.num_seqs, self.max_seqlen = num_seqs, max_seqlen
+
+
+def varlen_worklist(cu_seqlens: torch.Tensor, max_seqlen: int, block_m: int,
+                    cap: Optional[int] = None) -> Plan:
+    """Build the longest-first (segment, q-tile) list on the device."""
+    _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
+    n = cu_seqlens.numel() - 1
+    need = worklist_capacity(n, int(max_seqlen), int(block_m))
+    if need < 0:
+        raise ValueError("bad work-list sizes")
+    cap = need if cap is None else int(cap)
+    items = torch.empty((max(cap, 1), 2), dtype=torch.int32, device=cu_seqlens.device)
+    meta = torch.empty(2, dtype=torch.int32, device=cu_seqlens.device)
+    _lib.check(_lib.load().vit_varlen_worklist(
+        cu_seqlens.data_ptr(), n, int(max_seqlen), int(block_m), items.data_ptr(), cap,
+        meta.data_ptr(), _stream(cu_seqlens)))
+    return Plan(items, meta, cap, int(block_m), n, int(max_seqlen))
+
+
+def rebuild_worklist(plan: Plan, cu_seqlens: torch.Tensor) -> Plan:
+    """Rebuild ``plan`` in place for new ``cu_seqlens`` with the same segment count
+    and ``max_seqlen`` bound (no allocation)."""
+    _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
+    if cu_seqlens.numel() - 1 != plan.num_seqs:
+        raise ValueError("cu_seqlens has a different segment count than the plan")
+    _lib.check(_lib.load().vit_varlen_worklist(
+        cu_seqlens.data_ptr(), plan.num_seqs, plan.max_seqlen, plan.block_m, plan.items.data_ptr(),
+        plan.cap, plan.meta.data_ptr(), _stream(cu_seqlens)))
+    return plan
+
+
+def varlen_attn_planned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        cu_seqlens: torch.Tensor, plan: Plan, scale: Optional[float] = None,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Attention over a work-list from ``varlen_worklist`` (built with ``attn_block_m``)."""
+    _attn_checks(q, k, v, cu_seqlens)
+    T, H, D = q.shape
+    if plan.block_m != attn_block_m(H, D, q.dtype):
+        raise ValueError("plan was built with a different block_m than this kernel uses")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_cuda("out", out, q.dtype)
+    _lib.check(_lib.load().vit_varlen_attn_planned(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), plan.items.data_ptr(),
+        plan.cap, plan.meta.data_ptr(), H, D, float(scale), dtype_code(q.dtype), out.data_ptr(),
+        _stream(q)))
+    return out
+
+
+def device_error(reset: bool = False, device: Optional[torch.device] = None) -> int:
+    """Work-list error bits of the last ``varlen_attn`` on the current stream (syncs it)."""
+    import ctypes
+    stream = torch.cuda.current_stream(device).cuda_stream
+    err = ctypes.c_int32(0)
+    _lib.check(_lib.load().vit_device_error(stream, ctypes.byref(err), int(bool(reset))))
+    return int(err.value)
+
+
+def release() -> None:
+    _lib.load().vit_release()

@@ -7,30 +7,39 @@
 // cu_seqlens_q = cu_seqlens_k).  The S x S mask of VisionAttention.forward is
 // never formed: each workgroup only visits its own segment's keys.
 //
-// Design (one workgroup = 4 waves = 128 query rows of one head):
-//  * Each wave owns 32 query rows.  Its Q fragments stay in VGPRs for the
-//    whole key loop.
-//  * Keys stream through LDS in tiles of 64, double-buffered: the global loads
-//    of tile t+1 are issued before the math of tile t and written to the other
-//    LDS buffer after it, so one barrier per tile suffices.
+// Design (one workgroup = WAVES waves; each wave owns 32 query rows of one
+// head; two workgroups share a CU so one's softmax overlaps the other's MFMA):
+//  * Q fragments stay in VGPRs for the whole key loop.
+//  * K and V tiles of BN keys are copied global -> LDS by the buffer unit
+//    itself (buffer_load_dwordx4 ... lds) into a ring of STAGES buffers, issued
+//    STAGES-1 tiles ahead.  No VGPRs hold tiles in flight and no VALU stores
+//    them; each wave waits only on its own copies (vmcnt) and one barrier per
+//    tile publishes the tile to all waves.  The buffer resource is bounded by
+//    the segment, so keys past its end arrive as zeros.
 //  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: the query index then runs along the lanes, so
-//    the row max and row sum of the online softmax are in-lane reductions plus
-//    one exchange between the two 32-lane halves.
-//  * K rows are stored in LDS with bits 2 and 3 of the key index swapped.
-//    With that order the 32x32 accumulator layout hands each lane eight
-//    consecutive keys per 16-key step, which is exactly the B operand layout of
-//    the P V^T product, so P goes from the score registers to the next MFMA
-//    without any cross-lane shuffle.
-//  * O^T = V^T P^T is accumulated in fp32; V is transposed (4x4 blocks of
-//    bf16 in registers) on its way into LDS so each MFMA A fragment is one
-//    16-byte LDS read.
-//  * Softmax runs in base 2 on fp32 scores with the scale folded into one
-//    multiply: p = 2^(s*scale*log2(e) - m).
-//  * LDS rows are padded by 16 bytes (an odd number of 16-byte slots per row),
-//    so eight consecutive rows read at the same column hit distinct banks.
+//    v_mfma_f32_32x32x16_bf16: the query index runs along the lanes, so the row
+//    max and row sum of the online softmax are in-lane reductions plus one
+//    exchange between the two 32-lane halves.
+//  * K rows are placed in LDS with bits 2 and 3 of the key index swapped (the
+//    copy picks which key each LDS row receives).  With that order the 32x32
+//    accumulator layout hands each lane eight consecutive keys per 16-key step,
+//    which is the B operand layout of the P V^T product, so P goes from the
+//    score registers to the next MFMA without any cross-lane shuffle.
+//  * V stays row-major in LDS; the A operand of O^T = V^T P^T (eight
+//    consecutive keys of one head-dim column per lane) comes from two
+//    ds_read_b64_tr_b16 transpose reads.
+//  * LDS row strides, in 16-byte units: K rows use an odd count (eight rows
+//    read at the same column by ds_read_b128 hit distinct banks); V rows use
+//    2 mod 8 (the four rows x 32 bytes a transpose-read lane group touches hit
+//    distinct banks).
+//  * Softmax in base 2: p = 2^(s*c - m) with c = scale*log2(e), one FMA and
+//    one v_exp_f32 per score.  The reference max m is only raised (and O, l
+//    rescaled) when a tile's max exceeds it by more than kRescaleSlack, so
+//    p <= 2^kRescaleSlack and the rescale is skipped for almost every tile.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "vit_kernels.h"
 
@@ -41,66 +50,128 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) const u16 lds_u16_t;
 
-constexpr int kBM = kBlockMBf16;  // query rows per workgroup
-constexpr int kBN = 64;           // keys per LDS tile
-constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;     // log2 units: p stays <= 256
+constexpr int kRsrcWord3 = 0x00020000;    // gfx9-family buffer descriptor word 3 (raw, 32-bit)
+// Byte offset for copy lanes that fill padding: past any segment's num_records
+// (segments are limited to kMaxSegmentBytes) even after adding the tile offset.
+constexpr unsigned kPadOffset = 0x40000000u;
+static_assert(kMaxSegmentBytes <= (int64_t)kPadOffset, "pad offset must exceed every segment");
 
-template <int D>
+constexpr int odd_units(int u) { return (u & 1) ? u : u + 1; }
+constexpr int units_2_mod_8(int u) { return u + ((2 - u % 8) + 8) % 8; }
+
+template <int D_, int WAVES_, int BN_, int STAGES_, int OCC_>
 struct Cfg {
+  static constexpr int D = D_;
+  static constexpr int WAVES = WAVES_;
+  static constexpr int BN = BN_;                        // keys per tile
+  static constexpr int STAGES = STAGES_;                // LDS ring depth
+  static constexpr int OCC = OCC_;                      // waves per SIMD the kernel is built for
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BM = 32 * WAVES;                 // query rows per workgroup
+  static constexpr int KB = BN / 32;                    // 32-key blocks per tile
   static constexpr int KSTEPS = D / 16;                 // 16-wide contraction steps of Q K^T
   static constexpr int DB = (D + 31) / 32;              // 32-row blocks of O^T
-  static constexpr int DP = DB * 32;                    // head dim padded for the V^T tile
-  static constexpr int KROW = D + 8;                    // K tile row stride (elements)
-  static constexpr int VROW = kBN + 8;                  // V^T tile row stride (elements)
-  static constexpr int K_ELEMS = kBN * KROW;
-  static constexpr int V_ELEMS = DP * VROW;
-  static constexpr int LDS_ELEMS = 2 * (K_ELEMS + V_ELEMS);
-  static constexpr int KCH = kBN * D / 8;               // 16-byte chunks per K tile
-  static constexpr int KCH_PT = (KCH + kThreads - 1) / kThreads;
-  static constexpr int VUN = (kBN / 4) * (D / 4);       // 4 keys x 4 dims units per V tile
-  static constexpr int VUN_PT = (VUN + kThreads - 1) / kThreads;
+  static constexpr int DU = D / 8;                      // 16-byte units per row of data
+  static constexpr int KSTR = odd_units(DU);            // K row stride (units)
+  static constexpr int VSTR = units_2_mod_8(DU);        // V row stride (units)
+  static constexpr int NK = (BN * KSTR + 63) / 64;      // copy instructions for K
+  static constexpr int NV = (BN * VSTR + 63) / 64;      // copy instructions for V
+  static constexpr int NI = (NK + NV + WAVES - 1) / WAVES;  // copy instructions per wave
+  static constexpr int KREG = NK * 64;                  // K region (units), instruction aligned
+  // V region plus slack: dummy copies of surplus instruction slots land past
+  // the V rows, and the transpose reads of head-dim columns D..32*DB-1 read at
+  // most one row further.
+  static constexpr int VREG = (NI * WAVES - NK) * 64 + VSTR;
+  static constexpr int STAGE_UNITS = KREG + VREG;
+  static constexpr int LDS_BYTES = STAGES * STAGE_UNITS * 16;
   static_assert(D % 16 == 0, "head dim must be a multiple of 16");
+  static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
+  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+  static_assert(NI * (STAGES - 2) <= 63, "vmcnt range");
+  static_assert(LDS_BYTES * OCC <= 160 * 1024, "LDS budget");
 };
 
 __device__ __forceinline__ int swap_bits_2_3(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
-__device__ __forceinline__ unsigned int pack_lo(unsigned int a, unsigned int b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ unsigned int pack_hi(unsigned int a, unsigned int b) {
-  return (a >> 16) | (b & 0xffff0000u);
+// vmcnt(n) only (expcnt and lgkmcnt at their no-wait maxima), gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
+// One 64-lane global -> LDS copy of 16 bytes per lane: lane L writes LDS bytes
+// [lds_byte + 16L, lds_byte + 16L + 16).  Issued from asm so the compiler's
+// wait-counter pass does not drain it before every LDS read; the kernel waits
+// for its own copies explicitly.
+__device__ __forceinline__ void copy_to_lds(unsigned lds_byte, unsigned voffset, i32x4_t rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_byte), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, unsigned num_bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane(int(unsigned(a)));
+  r.y = __builtin_amdgcn_readfirstlane(int(unsigned(a >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane(int(num_bytes));
+  r.w = kRsrcWord3;
+  return r;
+}
+
+// p must point into LDS (a __shared__ array); the cast only changes the
+// address space the compiler sees.
+__device__ __forceinline__ i16x4_t ds_read_tr16(const u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds_u16_t*)p);
+}
+
+template <class C, bool POS_SCALE>
+__global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
     const int32_t* __restrict__ meta, int H, float scale_log2, u16* __restrict__ out) {
-  using C = Cfg<D>;
-  __shared__ __align__(16) u16 smem[C::LDS_ELEMS];
-  u16* const ks = smem;                    // [2][kBN][KROW], row p holds key swap_bits_2_3(p)
-  u16* const vts = smem + 2 * C::K_ELEMS;  // [2][DP][VROW], V^T
+  constexpr int D = C::D, BN = C::BN, KB = C::KB, STAGES = C::STAGES, NI = C::NI;
+  __shared__ __align__(16) u16 smem[C::LDS_BYTES / 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31;
   const int half = lane >> 5;
-  const size_t tok_stride = size_t(H) * D;
+  const int tok_stride = H * D;  // elements per token
+  const unsigned smem_base = static_cast<unsigned>((uintptr_t)(lds_u16_t*)smem);  // LDS address
 
-  // Rows D..DP-1 of the V^T tiles feed only output rows that are never
-  // stored; keep them finite.
-  if constexpr (C::DP != D) {
-    for (int i = tid; i < 2 * (C::DP - D) * C::VROW; i += kThreads) {
-      const int b = i / ((C::DP - D) * C::VROW);
-      const int r = i - b * (C::DP - D) * C::VROW;
-      vts[b * C::V_ELEMS + D * C::VROW + r] = 0;
-    }
+  // Per-lane byte offsets of this wave's copy instructions relative to the
+  // tile's first key.  Instruction slot i = wave + WAVES*j: K units first,
+  // then V units, then dummy slots that only write zeros into slack.
+  unsigned cp_off[NI];
+  bool cp_is_k[NI];
+  unsigned cp_lds[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int i = wave + C::WAVES * j;
+    const bool is_k = i < C::NK;
+    const int u = is_k ? i * 64 + lane : (i - C::NK) * 64 + lane;
+    const int str = is_k ? C::KSTR : C::VSTR;
+    const int row = u / str;
+    const int col = u - row * str;
+    const int key = is_k ? swap_bits_2_3(row) : row;
+    const bool data = row < BN && col < C::DU && i < C::NK + C::NV;
+    cp_off[j] = data ? unsigned((key * tok_stride + col * 8) * 2) : kPadOffset;
+    cp_is_k[j] = is_k;
+    cp_lds[j] = unsigned((is_k ? i * 64 : C::KREG + (i - C::NK) * 64) * 16);
   }
 
   const int64_t nunits = int64_t(meta[0]) * H;
@@ -111,209 +182,214 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const int qt = items[2 * item + 1];
     const int start = cu[seg];
     const int len = cu[seg + 1] - start;
-    const int qrow = qt * kBM + wave * 32 + l32;
-    const u16* const kbase = k + size_t(start) * tok_stride + size_t(h) * D;
-    const u16* const vbase = v + size_t(start) * tok_stride + size_t(h) * D;
+    // Offsets are 32-bit: a segment larger than the addressable span is skipped
+    // (the host rejects the max_seqlen that would allow it).
+    if (int64_t(len) * tok_stride * 2 > kMaxSegmentBytes) continue;
+    const int row0 = qt * C::BM + wave * 32;  // first query row of this wave
+    const bool wave_active = row0 < len;
+    const unsigned seg_bytes = unsigned(((len - 1) * tok_stride + D) * 2);
+    const i32x4_t krs = make_rsrc(k + size_t(start) * tok_stride + size_t(h) * D, seg_bytes);
+    const i32x4_t vrs = make_rsrc(v + size_t(start) * tok_stride + size_t(h) * D, seg_bytes);
 
     // Q^T fragments (B operand of S^T = K Q^T): lane holds 8 dims of its row.
     bf16x8_t qf[C::KSTEPS];
-    if (qrow < len) {
-      const u16* qp = q + size_t(start + qrow) * tok_stride + size_t(h) * D + half * 8;
+    {
+      const int row = row0 + l32;
+      if (row < len) {
+        const u16* qp = q + size_t(start + row) * tok_stride + size_t(h) * D + half * 8;
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s)
-        qf[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qp + s * 16));
-    } else {
+        for (int s = 0; s < C::KSTEPS; ++s)
+          qf[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qp + s * 16));
+      } else {
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) qf[s] = bf16x8_t{};
+        for (int s = 0; s < C::KSTEPS; ++s) qf[s] = bf16x8_t{};
+      }
     }
-
     f32x16_t o[C::DB];
 #pragma unroll
-    for (int b = 0; b < C::DB; ++b) o[b] = f32x16_t{};
-    float m_run = -INFINITY;  // running max of the scaled (log2-domain) scores
+    for (int d = 0; d < C::DB; ++d) o[d] = f32x16_t{};
+    float m_run = -INFINITY;  // reference max, log2 domain
     float l_run = 0.f;        // this lane's partial row sum
 
-    u32x4_t kreg[C::KCH_PT];
-    u32x2_t vreg[C::VUN_PT][4];
-
-    auto load_tile = [&](int kv0) {
-#pragma unroll
-      for (int i = 0; i < C::KCH_PT; ++i) {
-        const int c = tid + i * kThreads;
-        kreg[i] = u32x4_t{};
-        if (c < C::KCH) {
-          const int key = c / (D / 8);
-          const int dc = c - key * (D / 8);
-          if (kv0 + key < len)
-            kreg[i] = *reinterpret_cast<const u32x4_t*>(kbase + size_t(kv0 + key) * tok_stride + dc * 8);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < C::VUN_PT; ++i) {
-        const int u = tid + i * kThreads;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vreg[i][j] = u32x2_t{};
-        if (u < C::VUN) {
-          const int kq = u / (D / 4);
-          const int dq = u - kq * (D / 4);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = kv0 + 4 * kq + j;
-            if (key < len)
-              vreg[i][j] = *reinterpret_cast<const u32x2_t*>(vbase + size_t(key) * tok_stride + dq * 4);
-          }
-        }
-      }
-    };
-
-    auto store_tile = [&](int buf) {
-      u16* kdst = ks + buf * C::K_ELEMS;
-      u16* vdst = vts + buf * C::V_ELEMS;
-#pragma unroll
-      for (int i = 0; i < C::KCH_PT; ++i) {
-        const int c = tid + i * kThreads;
-        if (c < C::KCH) {
-          const int key = c / (D / 8);
-          const int dc = c - key * (D / 8);
-          *reinterpret_cast<u32x4_t*>(kdst + swap_bits_2_3(key) * C::KROW + dc * 8) = kreg[i];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < C::VUN_PT; ++i) {
-        const int u = tid + i * kThreads;
-        if (u < C::VUN) {
-          const int kq = u / (D / 4);
-          const int dq = u - kq * (D / 4);
-          u16* dst = vdst + (dq * 4) * C::VROW + kq * 4;
-          const u32x2_t* r = vreg[i];
-          // 4x4 transpose of bf16: row j = key 4kq+j, column e = dim 4dq+e.
-          *reinterpret_cast<u32x2_t*>(dst + 0 * C::VROW) =
-              u32x2_t{pack_lo(r[0].x, r[1].x), pack_lo(r[2].x, r[3].x)};
-          *reinterpret_cast<u32x2_t*>(dst + 1 * C::VROW) =
-              u32x2_t{pack_hi(r[0].x, r[1].x), pack_hi(r[2].x, r[3].x)};
-          *reinterpret_cast<u32x2_t*>(dst + 2 * C::VROW) =
-              u32x2_t{pack_lo(r[0].y, r[1].y), pack_lo(r[2].y, r[3].y)};
-          *reinterpret_cast<u32x2_t*>(dst + 3 * C::VROW) =
-              u32x2_t{pack_hi(r[0].y, r[1].y), pack_hi(r[2].y, r[3].y)};
-        }
-      }
-    };
-
-    const int ntiles = (len + kBN - 1) / kBN;
-    load_tile(0);
-    store_tile(0);
+    // Nothing of ours may be in flight when the copy pipeline starts counting,
+    // and the previous unit's last tile must no longer be read.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int t = 0; t < ntiles; ++t) {
-      const int buf = t & 1;
-      const int kv0 = t * kBN;
-      if (t + 1 < ntiles) load_tile(kv0 + kBN);
+    const int ntiles = (len + BN - 1) / BN;
+    auto issue_tile = [&](int t) {
+      const unsigned tile_off = unsigned(t) * unsigned(BN * 2) * unsigned(tok_stride);
+      const unsigned stage_lds = smem_base + unsigned((t % STAGES) * C::STAGE_UNITS * 16);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        copy_to_lds(stage_lds + cp_lds[j], cp_off[j] + tile_off, cp_is_k[j] ? krs : vrs);
+    };
+#pragma unroll
+    for (int t = 0; t < STAGES - 1; ++t)
+      if (t < ntiles) issue_tile(t);
 
-      // S^T = K Q^T for 64 keys: two 32-key blocks.
-      f32x16_t s[2];
-      const u16* kt = ks + buf * C::K_ELEMS + l32 * C::KROW + half * 8;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16_t{};
-#pragma unroll
-        for (int st = 0; st < C::KSTEPS; ++st) {
-          const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + kb * 32 * C::KROW + st * 16));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
-        }
+    // One key tile.  MASKED is true only for the last, partial tile.
+    auto process_tile = [&](auto masked_tag, int t) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      // Own copies of tile t done: at most min(STAGES-2, ntiles-1-t) later
+      // tiles' copies may still be in flight.
+      const int later = ntiles - 1 - t;
+      if constexpr (STAGES == 4) {
+        if (later >= 2) wait_vmcnt<NI * 2>();
+        else if (later == 1) wait_vmcnt<NI>();
+        else wait_vmcnt<0>();
+      } else if constexpr (STAGES == 3) {
+        if (later >= 1) wait_vmcnt<NI>();
+        else wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<0>();
       }
+      __syncthreads();  // everyone's copies of tile t landed; tile t-1 is free
+      if (t + STAGES - 1 < ntiles) issue_tile(t + STAGES - 1);
 
-      // Online softmax.  Register r of block kb holds key
-      // kv0 + 32kb + 16(r>>3) + 8half + (r&7) for query row l32.
-      float mt = -INFINITY;
-      const bool partial = kv0 + kBN > len;
+      if (wave_active) {
+        const int kv0 = t * BN;
+        const u16* stage = smem + (t % STAGES) * C::STAGE_UNITS * 8;
+        // S^T = K Q^T.
+        f32x16_t s[KB];
+        const u16* kt = stage + l32 * C::KSTR * 8 + half * 8;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
+          s[kb] = f32x16_t{};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r] * scale_log2;
-          if (partial) {
-            const int key = kv0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
-            if (key >= len) x = -INFINITY;
-          }
-          s[kb][r] = x;
-          mt = fmaxf(mt, x);
-        }
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float rsum = 0.f;
-      bf16x8_t p[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(s[kb][r] - m_new);
-          rsum += e;
-          p[kb][r >> 3][r & 7] = (__bf16)e;
-        }
-      }
-      l_run = l_run * alpha + rsum;
-#pragma unroll
-      for (int b = 0; b < C::DB; ++b) o[b] *= alpha;
-
-      // O^T += V^T P^T.
-      const u16* vt = vts + buf * C::V_ELEMS + l32 * C::VROW + half * 8;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-          for (int b = 0; b < C::DB; ++b) {
+          for (int st = 0; st < C::KSTEPS; ++st) {
             const bf16x8_t a = __builtin_bit_cast(
-                bf16x8_t,
-                *reinterpret_cast<const u32x4_t*>(vt + b * 32 * C::VROW + kb * 32 + s2 * 16));
-            o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[kb][s2], o[b], 0, 0, 0);
+                bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + kb * 32 * C::KSTR * 8 + st * 16));
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
+          }
+        }
+
+        __builtin_amdgcn_sched_barrier(0);
+        // Online softmax.  Register r of block kb holds key
+        // kv0 + 32kb + 16(r>>3) + 8half + (r&7) for query row l32.
+        bf16x8_t p[KB][2];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x = POS_SCALE ? s[kb][r] : s[kb][r] * scale_log2;
+            if constexpr (MASKED) {
+              const int key = kv0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
+              if (key >= len) x = -INFINITY;
+            }
+            s[kb][r] = x;
+            mx = fmaxf(mx, x);
+          }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mt = POS_SCALE ? mx * scale_log2 : mx;  // tile max, log2 domain
+        if (__any(mt > m_run + kRescaleSlack)) {
+          const float m_new = fmaxf(m_run, mt);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int d = 0; d < C::DB; ++d) o[d] *= alpha;
+        }
+        const float neg_m = -m_run;
+        float rsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = POS_SCALE ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, neg_m))
+                                      : __builtin_amdgcn_exp2f(s[kb][r] + neg_m);
+            rsum += e;
+            p[kb][r >> 3][r & 7] = (__bf16)e;
+          }
+        }
+        l_run += rsum;
+
+        __builtin_amdgcn_sched_barrier(0);
+        // O^T += V^T P^T.  Transpose-read lane l (group g = l>>4, j = l&15)
+        // addresses V row (key) kb*32 + 16*s2 + 8*half + 4*qh + (j>>2), dims
+        // 32d + 16*(g&1) + 4*(j&3) .. +3, and receives keys
+        // kb*32 + 16*s2 + 8*half + 4*qh + 0..3 of dim 32d + (l&31).
+        const u16* vst = stage + C::KREG * 8;
+        const int vrow = 8 * half + ((lane & 15) >> 2);
+        const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+            for (int d = 0; d < C::DB; ++d) {
+              const u16* base = vst + (kb * 32 + 16 * s2 + vrow) * C::VSTR * 8 + 32 * d + vcol;
+              const i16x4_t a8[2] = {ds_read_tr16(base), ds_read_tr16(base + 4 * C::VSTR * 8)};
+              const bf16x8_t a = __builtin_bit_cast(bf16x8_t, a8);
+              o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[kb][s2], o[d], 0, 0, 0);
+            }
           }
         }
       }
+    };
 
-      if (t + 1 < ntiles) store_tile(buf ^ 1);
-      __syncthreads();
-    }
+    const int nfull = len / BN;
+    for (int t = 0; t < nfull; ++t) process_tile(std::false_type{}, t);
+    if (nfull < ntiles) process_tile(std::true_type{}, nfull);
 
-    // Finalize: O^T register r of block b holds dim 32b + 8(r>>2) + 4half + (r&3).
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.f / l_tot;
-    if (qrow < len) {
-      u16* op = out + size_t(start + qrow) * tok_stride + size_t(h) * D;
+    // Finalize: O^T register r of block d holds dim 32d + 8(r>>2) + 4half + (r&3).
+    {
+      const int row = row0 + l32;
+      const float l_tot = l_run + __shfl_xor(l_run, 32);
+      if (row < len) {
+        const float inv = 1.f / l_tot;
+        u16* op = out + size_t(start + row) * tok_stride + size_t(h) * D;
 #pragma unroll
-      for (int b = 0; b < C::DB; ++b) {
+        for (int d = 0; d < C::DB; ++d) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = b * 32 + 8 * g + 4 * half;
-          if (d0 < D) {
-            __bf16 w[4];
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = d * 32 + 8 * g + 4 * half;
+            if (d0 < D) {
+              __bf16 w[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[b][4 * g + e] * inv);
-            *reinterpret_cast<u32x2_t*>(op + d0) = __builtin_bit_cast(u32x2_t, w);
+              for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[d][4 * g + e] * inv);
+              *reinterpret_cast<u32x2_t*>(op + d0) = __builtin_bit_cast(u32x2_t, w);
+            }
           }
         }
       }
     }
-    __syncthreads();  // LDS is reused by the next unit
   }
 }
+
+template <class C>
+hipError_t launch_cfg(const void* q, const void* k, const void* v, const int32_t* cu,
+                      const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
+                      void* out, hipStream_t stream) {
+  const int64_t units = cap * int64_t(H);
+  if (units <= 0) return hipSuccess;
+  const int64_t grid = units < kMaxAttnGrid ? units : kMaxAttnGrid;
+  const float c = scale * kLog2e;
+  auto kern = c > 0.f ? attn_bf16_kernel<C, true> : attn_bf16_kernel<C, false>;
+  hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), 0, stream,
+                     static_cast<const u16*>(q), static_cast<const u16*>(k),
+                     static_cast<const u16*>(v), cu, items, meta, H, c, static_cast<u16*>(out));
+  return hipGetLastError();
+}
+
+// Per head dim: (waves, keys per tile, ring depth, waves per SIMD).  Rows per
+// workgroup must equal bf16_block_m_const(D).
+template <int D> struct Choice;
+template <> struct Choice<32> { using C = Cfg<32, 4, 64, 3, 2>; };
+template <> struct Choice<64> { using C = Cfg<64, 4, 64, 3, 2>; };
+template <> struct Choice<80> { using C = Cfg<80, 4, 64, 3, 2>; };
+template <> struct Choice<96> { using C = Cfg<96, 4, 32, 4, 2>; };
+template <> struct Choice<128> { using C = Cfg<128, 4, 32, 3, 2>; };
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* cu,
                     const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
                     void* out, hipStream_t stream) {
-  int64_t units = cap * int64_t(H);
-  if (units <= 0) return hipSuccess;
-  const int64_t grid = units < kMaxAttnGrid ? units : kMaxAttnGrid;
-  hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3(unsigned(grid)), dim3(kThreads), 0, stream,
-                     static_cast<const u16*>(q), static_cast<const u16*>(k),
-                     static_cast<const u16*>(v), cu, items, meta, H, scale * kLog2e,
-                     static_cast<u16*>(out));
-  return hipGetLastError();
+  using C = typename Choice<D>::C;
+  static_assert(C::BM == bf16_block_m_const(D), "work-list block size mismatch");
+  return launch_cfg<C>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
 }
 
 }  // namespace

@@ -102,15 +102,20 @@ int check_attn_args(const void* q, const void* k, const void* v, const int32_t* 
   return VIT_OK;
 }
 
-int block_m_for(int dtype) { return dtype == VIT_BF16 ? vit::kBlockMBf16 : vit::kBlockMF32; }
+int block_m_for(int dtype, int D) {
+  return dtype == VIT_BF16 ? vit::bf16_block_m_const(D) : vit::kBlockMF32;
+}
 
 int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, int num_seqs,
                 int max_seqlen, int H, int D, float scale, void* out, hipStream_t stream,
                 int dtype) {
   int rc = check_attn_args(q, k, v, cu, num_seqs, max_seqlen, H, D, scale, out);
   if (rc != VIT_OK) return rc;
+  if (int64_t(max_seqlen) * H * D * 2 > vit::kMaxSegmentBytes)
+    return fail(VIT_ERR_UNSUPPORTED, "max_seqlen * num_heads * head_dim * 2 bytes exceeds %lld",
+                (long long)vit::kMaxSegmentBytes);
   if (num_seqs == 0 || max_seqlen == 0) return ok();
-  const int bm = block_m_for(dtype);
+  const int bm = block_m_for(dtype, D);
   const int64_t cap = capacity(num_seqs, max_seqlen, bm);
   if (cap > kMaxCapacity) return fail(VIT_ERR_UNSUPPORTED, "work-list capacity %lld too large", (long long)cap);
   Scratch* s = nullptr;
@@ -182,7 +187,7 @@ int vit_attn_block_m(int num_heads, int head_dim, int dtype) {
     return -fail(VIT_ERR_UNSUPPORTED, "head_dim %d not supported", head_dim);
   if (dtype != VIT_F32 && dtype != VIT_BF16) return -fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   ok();
-  return block_m_for(dtype);
+  return block_m_for(dtype, head_dim);
 }
 
 int64_t vit_worklist_capacity(int num_seqs, int max_seqlen, int block_m) {

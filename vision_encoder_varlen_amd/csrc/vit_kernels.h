@@ -8,11 +8,18 @@
 namespace vit {
 
 // Query rows per (segment, q-tile) work item.
-constexpr int kBlockMBf16 = 128;  // 4 waves x 32 rows, bf16 MFMA kernel
-constexpr int kBlockMF32 = 32;    // 1 wave, lane pairs share a row, fp32 kernel
+// bf16 MFMA kernel: 4 waves x 32 rows.
+constexpr int bf16_block_m_const(int /*head_dim*/) { return 128; }
+constexpr int kBlockMF32 = 32;  // 1 wave, lane pairs share a row, fp32 kernel
 
 // Work-list builder limits: one workgroup sorts every segment in LDS.
 constexpr int kWorklistMaxSeqs = 8192;
+
+// Largest span of one segment's rows in a q, k or v tensor (bytes) that the
+// bf16 attention kernel addresses with 32-bit buffer offsets.  Segments whose
+// len * H * D * 2 exceeds it are skipped by the kernel; the C ABI rejects
+// max_seqlen values that allow them.
+constexpr int64_t kMaxSegmentBytes = int64_t(1) << 30;
 
 // Upper bound on attention workgroups per launch; larger work loops inside.
 constexpr int64_t kMaxAttnGrid = int64_t(1) << 22;

@@ -8,9 +8,10 @@ Default workload: 4 images of 32x32 patches (4096 tokens), 16 heads, head dim
 80, bf16, RoPE only (the workload the attention metric is quoted on).  The
 metric is attention TFLOP/s with FLOPs = 4*H*D*sum(s_i^2) per step.
 
-The attention kernel's own average duration is measured live with HIP events
-around its launch inside the timed loop, on the stream it is launched on; the
-roofline fraction is taken against MI355X's dense bf16 MFMA peak.  The CPU
+The attention kernel's own average duration is measured live inside the timed
+loop with HIP events that the kernel's dispatch records at its start and end
+(hipExtLaunchKernel, on the stream it is launched on); the roofline fraction is
+taken against MI355X's dense bf16 MFMA peak.  The CPU
 oracle is timed on a bounded sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N]
@@ -45,9 +46,77 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU-oracle time budget")
-    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attn_traffic.json"),
-                   help="HBM traffic per attention launch measured by rocprofv3 counters")
+    p.add_argument("--traffic-json", default="",
+                   help="HBM traffic per attention launch measured by rocprofv3 counters "
+                        "(default profiles/attn_traffic_<workload>.json)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="run one device-to-device copy of MIB MiB before warm-up, as the known-size "
+                        "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU: turn the counter_collection.csv files of a FETCH_SIZE pass and a "
+                        "WRITE_SIZE pass (over a run with --copy-calibration) into --traffic-json")
+    p.add_argument("--calibration-meta", default="", metavar="JSON",
+                   help="with --copy-calibration: where to write the copy size and workload; "
+                        "with --summarize-pmc: where to read them")
+    p.add_argument("--pmc-command", default="",
+                   help="with --summarize-pmc: the profiling command, stored with the result")
     return p.parse_args()
+
+
+def _counter_rows(path, counter):
+    """(kernel name, grid size, value in KiB) per dispatch of one rocprofv3 counter CSV."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_pmc(args):
+    """HBM bytes per attention launch from two counter passes.
+
+    Each counter is scaled by the factor that makes it read the known size of
+    the calibration copy (the largest copy-kernel dispatch of the run), so the
+    result is in bytes whatever unit and coverage the counter has."""
+    fetch = _counter_rows(args.summarize_pmc[0], "FETCH_SIZE")
+    write = _counter_rows(args.summarize_pmc[1], "WRITE_SIZE")
+
+    def calib(rows):
+        copies = [r for r in rows if "copy" in r[0].lower()]
+        if not copies:
+            raise SystemExit("no copy-kernel dispatch in the counter CSV (run with --copy-calibration)")
+        return max(c[2] for c in copies)
+
+    def attn(rows):
+        vals = [r[2] for r in rows if "attn_bf16_kernel" in r[0] or "attn_f32_kernel" in r[0]]
+        if not vals:
+            raise SystemExit("no attention dispatch in the counter CSV")
+        return float(np.mean(vals)), len(vals)
+
+    meta = json.load(open(args.calibration_meta))
+    known_kib = meta["copy_mib"] * 1024.0
+    f_fetch = known_kib / calib(fetch)
+    f_write = known_kib / calib(write)
+    fk, nf = attn(fetch)
+    wk, nw = attn(write)
+    res = {
+        "workload": meta["workload"],
+        "kernel_source_sha": meta["kernel_source_sha"],
+        "bytes_per_launch": round((fk * f_fetch + wk * f_write) * 1024.0),
+        "fetch_bytes_per_launch": round(fk * f_fetch * 1024.0),
+        "write_bytes_per_launch": round(wk * f_write * 1024.0),
+        "algorithmic_bytes_per_launch": meta["algorithmic_bytes"],
+        "raw_kib_per_launch": {"FETCH_SIZE": fk, "WRITE_SIZE": wk},
+        "calibration": {"copy_mib": meta["copy_mib"], "fetch_factor": f_fetch, "write_factor": f_write},
+        "dispatches": {"FETCH_SIZE": nf, "WRITE_SIZE": nw},
+        "command": args.pmc_command,
+    }
+    with open(args.traffic_json or _traffic_path(meta["workload"]), "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res))
 
 
 def cpu_baseline(wl, x, budget_s):
@@ -82,6 +151,9 @@ def cpu_baseline(wl, x, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path runs on a "
               "single GPU; see DESIGN.md for how it would shard).", file=sys.stderr)
@@ -127,8 +199,29 @@ def main():
                out.data_ptr(), sh)
     f_pre, f_wl, f_at = lib.vit_qk_norm_rope, lib.vit_varlen_worklist, lib.vit_varlen_attn_planned
 
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        if args.calibration_meta:
+            with open(args.calibration_meta, "w") as f:
+                json.dump({"copy_mib": args.copy_calibration, "workload": wl.name,
+                           "kernel_source_sha": _kernel_sha(),
+                           "algorithmic_bytes": 4 * T * H * D * q.element_size()}, f)
+
     K, Wm = args.steps, args.warmup
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+
+    # Create every HIP event up front (torch creates them on first record).
+    for e in ev:
+        for x_ in e:
+            x_.record(stream)
+    torch.cuda.synchronize()
+    f_hook = lib.vit_time_next_attention
 
     def step(e=None):
         if e is not None:
@@ -136,10 +229,9 @@ def main():
         check(f_pre(*pre_args))
         check(f_wl(*wl_args))
         if e is not None:
-            e[1].record(stream)
+            # e[1] / e[2]: the attention kernel's own dispatch start and end.
+            check(f_hook(e[1].cuda_event, e[2].cuda_event))
         check(f_at(*at_args))
-        if e is not None:
-            e[2].record(stream)
 
     for _ in range(Wm):
         step()
@@ -169,9 +261,10 @@ def main():
     is_bf16 = wl.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if is_bf16 else PEAK_F32_VALU_TFLOPS
     traffic = None
-    if os.path.exists(args.traffic_json):
+    tpath = args.traffic_json or _traffic_path(wl.name)
+    if os.path.exists(tpath):
         try:
-            tj = json.load(open(args.traffic_json))
+            tj = json.load(open(tpath))
             if tj.get("workload") == wl.name and tj.get("kernel_source_sha") == _kernel_sha():
                 traffic = tj.get("bytes_per_launch")
         except Exception:
@@ -199,13 +292,17 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "avg_launch_us": round(attn_avg_ms * 1e3, 3)},
         "kernels_us": {"attention": round(attn_avg_ms * 1e3, 3),
-                       "prepass_plus_worklist": round(float(front_ms.mean()) * 1e3, 3),
+                       "prepass_worklist_and_gaps": round(float(front_ms.mean()) * 1e3, 3),
                        "prepass_bytes": pre_bytes},
         "step_frac_of_peak": round(value / peak, 4),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"attn_traffic_{workload}.json")
 
 
 def _kernel_sha():

@@ -172,6 +172,20 @@ int vit_device_error(hipStream_t stream, int32_t* err, int reset);
 /* Message of the last failed call on this thread ("" if none). */
 const char* vit_last_error(void);
 
+/*
+ * Timing hook for profilers and benchmarks.  The next call on this host thread
+ * of vit_varlen_attn, vit_varlen_attn_f32 or vit_varlen_attn_planned records
+ * `start` when its attention kernel's dispatch begins and `stop` when it ends
+ * (hipExtLaunchKernel's dispatch timestamps: the kernel alone, without launch
+ * gaps); the hook is then cleared, whether that call succeeds or not.  A call
+ * that launches no kernel records both events back to back on its stream.
+ * The work-list launch made inside vit_varlen_attn* is not timed.
+ *  start, stop: events created with timing enabled, owned by the caller, or
+ *               both null to clear the hook.
+ * Returns VIT_ERR_INVALID_ARG when exactly one of them is null.
+ */
+int vit_time_next_attention(hipEvent_t start, hipEvent_t stop);
+
 /* Frees all library-owned scratch on every device (synchronises each device first). */
 void vit_release(void);
 

@@ -179,3 +179,31 @@ def test_errors_raise_value_error():
     cu = torch.tensor([0, 4], dtype=torch.int32, device="cuda")
     with pytest.raises(ValueError, match="head_dim"):
         ops.varlen_attn(q, q.clone(), q.clone(), cu, 4)
+
+
+@pytest.mark.parametrize("D", [80, 128])
+def test_logit_jump_after_first_tile(D):
+    """Keys after the first tile score far above every key of the first tile
+    (a jump of several hundred logits), so the kernel's running reference max
+    must move after it was first used."""
+    rng = np.random.default_rng(13)
+    lens = [300, 97]
+    wl = W.from_seqlens(lens, H=2, D=D, dtype="bf16", seed=13)
+    x = W.generate(wl)
+    u = np.zeros(D, dtype=np.float32)
+    u[: D // 2] = 1.0
+    u /= np.linalg.norm(u)
+    big = 4.0 * np.sqrt(D)                      # |q| = |k| = 4 sqrt(D): logits ~ +-16 D * scale
+    q = np.broadcast_to(big * u, (sum(lens), 2, D)).copy()
+    k = x.k.copy() * 0.01
+    k[:40] -= big * u                          # first tile of each head: strongly negative
+    k[300:310] -= big * u
+    k[60:] += big * u * (rng.random((sum(lens) - 60, 1, 1)) > 0.5)
+    x.q = q.astype(np.float32)
+    x.k = k.astype(np.float32)
+    from vision_encoder_varlen_amd.workloads import bf16_bits_to_f32, f32_to_bf16_bits
+    x.q = bf16_bits_to_f32(f32_to_bf16_bits(x.q)).reshape(x.q.shape)
+    x.k = bf16_bits_to_f32(f32_to_bf16_bits(x.k)).reshape(x.k.shape)
+    got, _ = _gpu_attn(x, wl)
+    want = oracle.varlen_attention(x.q, x.k, x.v, x.cu_seqlens, wl.softmax_scale)
+    assert_attn_close(got, want, "bf16", f"logit jump D={D}")

@@ -36,6 +36,7 @@
 //    one v_exp_f32 per score.  The reference max m is only raised (and O, l
 //    rescaled) when a tile's max exceeds it by more than kRescaleSlack, so
 //    p <= 2^kRescaleSlack and the rescale is skipped for almost every tile.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -84,20 +85,31 @@ struct Cfg {
   static constexpr int VSTR = units_2_mod_8(DU);        // V row stride (units)
   static constexpr int NK = (BN * KSTR + 63) / 64;      // copy instructions for K
   static constexpr int NV = (BN * VSTR + 63) / 64;      // copy instructions for V
-  static constexpr int NI = (NK + NV + WAVES - 1) / WAVES;  // copy instructions per wave
+  static constexpr int NT = NK + NV;                    // copy instructions per tile
+  // Instruction i goes to wave i % WAVES: the first NT % WAVES waves issue
+  // NI_HI copies per tile, the others NI_LO.
+  static constexpr int NI_LO = NT / WAVES;
+  static constexpr int NI_HI = (NT + WAVES - 1) / WAVES;
   static constexpr int KREG = NK * 64;                  // K region (units), instruction aligned
-  // V region plus slack: dummy copies of surplus instruction slots land past
-  // the V rows, and the transpose reads of head-dim columns D..32*DB-1 read at
-  // most one row further.
-  static constexpr int VREG = (NI * WAVES - NK) * 64 + VSTR;
+  // V region plus slack: the last copy instruction may run past the V rows,
+  // and the transpose reads of head-dim columns D..32*DB-1 read at most one
+  // row further.
+  static constexpr int VREG = NV * 64 + VSTR;
   static constexpr int STAGE_UNITS = KREG + VREG;
   static constexpr int LDS_BYTES = STAGES * STAGE_UNITS * 16;
   static_assert(D % 16 == 0, "head dim must be a multiple of 16");
   static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
-  static_assert(NI * (STAGES - 2) <= 63, "vmcnt range");
+  static_assert(NI_HI * (STAGES - 2) <= 63, "vmcnt range");
   static_assert(LDS_BYTES * OCC <= 160 * 1024, "LDS budget");
 };
+
+// The value lane l ^ 32 holds (v_permlane32_swap: a VALU exchange of the two
+// 32-lane halves, no LDS round trip).
+__device__ __forceinline__ float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(threadIdx.x & 32 ? r[0] : r[1]);
+}
 
 __device__ __forceinline__ int swap_bits_2_3(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
@@ -108,6 +120,19 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most `later` tiles of this wave's copies (NI instructions
+// each) are still in flight.
+template <int NI, int STAGES>
+__device__ __forceinline__ void wait_copies(int later) {
+  if constexpr (STAGES >= 4) {
+    if (later >= 2) { wait_vmcnt<NI * 2>(); return; }
+  }
+  if constexpr (STAGES >= 3) {
+    if (later >= 1) { wait_vmcnt<NI>(); return; }
+  }
+  wait_vmcnt<0>();
 }
 
 // One 64-lane global -> LDS copy of 16 bytes per lane: lane L writes LDS bytes
@@ -133,8 +158,8 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, unsigned num_byte
 
 // p must point into LDS (a __shared__ array); the cast only changes the
 // address space the compiler sees.
-__device__ __forceinline__ i16x4_t ds_read_tr16(const u16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds_u16_t*)p);
+__device__ __forceinline__ i16x4_t ds_read_tr16(lds_u16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
 }
 
 template <class C, bool POS_SCALE>
@@ -142,7 +167,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
     const int32_t* __restrict__ meta, int H, float scale_log2, u16* __restrict__ out) {
-  constexpr int D = C::D, BN = C::BN, KB = C::KB, STAGES = C::STAGES, NI = C::NI;
+  constexpr int D = C::D, BN = C::BN, KB = C::KB, STAGES = C::STAGES, NI = C::NI_HI;
   __shared__ __align__(16) u16 smem[C::LDS_BYTES / 2];
 
   const int tid = threadIdx.x;
@@ -154,8 +179,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
   const unsigned smem_base = static_cast<unsigned>((uintptr_t)(lds_u16_t*)smem);  // LDS address
 
   // Per-lane byte offsets of this wave's copy instructions relative to the
-  // tile's first key.  Instruction slot i = wave + WAVES*j: K units first,
-  // then V units, then dummy slots that only write zeros into slack.
+  // tile's first key.  Instruction i = wave + WAVES*j (K units first, then V
+  // units); lanes that fall on row padding get an offset past num_records and
+  // write zeros.
+  const bool wave_hi = wave < C::NT % C::WAVES || C::NT % C::WAVES == 0;
   unsigned cp_off[NI];
   bool cp_is_k[NI];
   unsigned cp_lds[NI];
@@ -168,7 +195,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     const int row = u / str;
     const int col = u - row * str;
     const int key = is_k ? swap_bits_2_3(row) : row;
-    const bool data = row < BN && col < C::DU && i < C::NK + C::NV;
+    const bool data = row < BN && col < C::DU;
     cp_off[j] = data ? unsigned((key * tok_stride + col * 8) * 2) : kPadOffset;
     cp_is_k[j] = is_k;
     cp_lds[j] = unsigned((is_k ? i * 64 : C::KREG + (i - C::NK) * 64) * 16);
@@ -222,7 +249,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       const unsigned stage_lds = smem_base + unsigned((t % STAGES) * C::STAGE_UNITS * 16);
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        copy_to_lds(stage_lds + cp_lds[j], cp_off[j] + tile_off, cp_is_k[j] ? krs : vrs);
+        if (j < C::NI_LO || wave_hi)
+          copy_to_lds(stage_lds + cp_lds[j], cp_off[j] + tile_off, cp_is_k[j] ? krs : vrs);
     };
 #pragma unroll
     for (int t = 0; t < STAGES - 1; ++t)
@@ -233,38 +261,58 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       constexpr bool MASKED = decltype(masked_tag)::value;
       // Own copies of tile t done: at most min(STAGES-2, ntiles-1-t) later
       // tiles' copies may still be in flight.
-      const int later = ntiles - 1 - t;
-      if constexpr (STAGES == 4) {
-        if (later >= 2) wait_vmcnt<NI * 2>();
-        else if (later == 1) wait_vmcnt<NI>();
-        else wait_vmcnt<0>();
-      } else if constexpr (STAGES == 3) {
-        if (later >= 1) wait_vmcnt<NI>();
-        else wait_vmcnt<0>();
-      } else {
-        wait_vmcnt<0>();
-      }
+      const int later = min(ntiles - 1 - t, STAGES - 2);
+      if (wave_hi) wait_copies<C::NI_HI, STAGES>(later);
+      else wait_copies<C::NI_LO, STAGES>(later);
       __syncthreads();  // everyone's copies of tile t landed; tile t-1 is free
       if (t + STAGES - 1 < ntiles) issue_tile(t + STAGES - 1);
 
       if (wave_active) {
         const int kv0 = t * BN;
         const u16* stage = smem + (t % STAGES) * C::STAGE_UNITS * 8;
+        // All LDS fragment reads of the tile are issued up front, K first, so
+        // their latency is paid once and the V reads land during the scores
+        // and the softmax.
+        bf16x8_t kf[KB][C::KSTEPS];
+        const u16* kt = stage + l32 * C::KSTR * 8 + half * 8;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int st = 0; st < C::KSTEPS; ++st)
+            kf[kb][st] = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + kb * 32 * C::KSTR * 8 + st * 16));
+        // Transpose-read lane l (group g = l>>4, j = l&15) addresses V row (key)
+        // kb*32 + 16*s2 + 8*half + 4*qh + (j>>2), dims 32d + 16*(g&1) +
+        // 4*(j&3) .. +3, and receives keys kb*32 + 16*s2 + 8*half + 4*qh + 0..3
+        // of dim 32d + (l&31).  One LDS-space base; the per-read offsets are
+        // constants the compiler folds into the instructions.
+        lds_u16_t* const vbase = (lds_u16_t*)(stage + C::KREG * 8) +
+                                 (8 * half + ((lane & 15) >> 2)) * C::VSTR * 8 +
+                                 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        i16x4_t vf[KB][2][C::DB][2];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int d = 0; d < C::DB; ++d) {
+              lds_u16_t* base = vbase + (kb * 32 + 16 * s2) * C::VSTR * 8 + 32 * d;
+              vf[kb][s2][d][0] = ds_read_tr16(base);
+              vf[kb][s2][d][1] = ds_read_tr16(base + 4 * C::VSTR * 8);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+
         // S^T = K Q^T.
         f32x16_t s[KB];
-        const u16* kt = stage + l32 * C::KSTR * 8 + half * 8;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           s[kb] = f32x16_t{};
 #pragma unroll
-          for (int st = 0; st < C::KSTEPS; ++st) {
-            const bf16x8_t a = __builtin_bit_cast(
-                bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + kb * 32 * C::KSTR * 8 + st * 16));
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
-          }
+          for (int st = 0; st < C::KSTEPS; ++st)
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][st], qf[st], s[kb], 0, 0, 0);
         }
-
         __builtin_amdgcn_sched_barrier(0);
+
         // Online softmax.  Register r of block kb holds key
         // kv0 + 32kb + 16(r>>3) + 8half + (r&7) for query row l32.
         bf16x8_t p[KB][2];
@@ -282,7 +330,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
             mx = fmaxf(mx, x);
           }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = fmaxf(mx, other_half(mx));
         const float mt = POS_SCALE ? mx * scale_log2 : mx;  // tile max, log2 domain
         if (__any(mt > m_run + kRescaleSlack)) {
           const float m_new = fmaxf(m_run, mt);
@@ -293,40 +341,29 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
           for (int d = 0; d < C::DB; ++d) o[d] *= alpha;
         }
         const float neg_m = -m_run;
-        float rsum = 0.f;
+        float part[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float e = POS_SCALE ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, neg_m))
                                       : __builtin_amdgcn_exp2f(s[kb][r] + neg_m);
-            rsum += e;
+            part[r & 3] += e;
             p[kb][r >> 3][r & 7] = (__bf16)e;
           }
         }
-        l_run += rsum;
-
+        l_run += (part[0] + part[1]) + (part[2] + part[3]);
         __builtin_amdgcn_sched_barrier(0);
-        // O^T += V^T P^T.  Transpose-read lane l (group g = l>>4, j = l&15)
-        // addresses V row (key) kb*32 + 16*s2 + 8*half + 4*qh + (j>>2), dims
-        // 32d + 16*(g&1) + 4*(j&3) .. +3, and receives keys
-        // kb*32 + 16*s2 + 8*half + 4*qh + 0..3 of dim 32d + (l&31).
-        const u16* vst = stage + C::KREG * 8;
-        const int vrow = 8 * half + ((lane & 15) >> 2);
-        const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+        // O^T += V^T P^T.
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
+          for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-            for (int d = 0; d < C::DB; ++d) {
-              const u16* base = vst + (kb * 32 + 16 * s2 + vrow) * C::VSTR * 8 + 32 * d + vcol;
-              const i16x4_t a8[2] = {ds_read_tr16(base), ds_read_tr16(base + 4 * C::VSTR * 8)};
-              const bf16x8_t a = __builtin_bit_cast(bf16x8_t, a8);
-              o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[kb][s2], o[d], 0, 0, 0);
-            }
-          }
-        }
+            for (int d = 0; d < C::DB; ++d)
+              o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8_t, vf[kb][s2][d]), p[kb][s2], o[d], 0, 0, 0);
       }
     };
 
@@ -337,7 +374,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     // Finalize: O^T register r of block d holds dim 32d + 8(r>>2) + 4half + (r&3).
     {
       const int row = row0 + l32;
-      const float l_tot = l_run + __shfl_xor(l_run, 32);
+      const float l_tot = l_run + other_half(l_run);
       if (row < len) {
         const float inv = 1.f / l_tot;
         u16* op = out + size_t(start + row) * tok_stride + size_t(h) * D;
@@ -362,13 +399,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
 template <class C>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, const int32_t* cu,
                       const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
-                      void* out, hipStream_t stream) {
+                      void* out, hipStream_t stream, hipEvent_t e0,
+                    hipEvent_t e1) {
   const int64_t units = cap * int64_t(H);
   if (units <= 0) return hipSuccess;
   const int64_t grid = units < kMaxAttnGrid ? units : kMaxAttnGrid;
   const float c = scale * kLog2e;
   auto kern = c > 0.f ? attn_bf16_kernel<C, true> : attn_bf16_kernel<C, false>;
-  hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), 0, stream,
+  hipExtLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), 0, stream, e0, e1, 0,
                      static_cast<const u16*>(q), static_cast<const u16*>(k),
                      static_cast<const u16*>(v), cu, items, meta, H, c, static_cast<u16*>(out));
   return hipGetLastError();
@@ -377,32 +415,34 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const int32_t
 // Per head dim: (waves, keys per tile, ring depth, waves per SIMD).  Rows per
 // workgroup must equal bf16_block_m_const(D).
 template <int D> struct Choice;
-template <> struct Choice<32> { using C = Cfg<32, 4, 64, 3, 2>; };
-template <> struct Choice<64> { using C = Cfg<64, 4, 64, 3, 2>; };
-template <> struct Choice<80> { using C = Cfg<80, 4, 64, 3, 2>; };
+template <> struct Choice<32> { using C = Cfg<32, 4, 32, 3, 2>; };
+template <> struct Choice<64> { using C = Cfg<64, 4, 32, 3, 2>; };
+template <> struct Choice<80> { using C = Cfg<80, 4, 64, 2, 2>; };
 template <> struct Choice<96> { using C = Cfg<96, 4, 32, 4, 2>; };
-template <> struct Choice<128> { using C = Cfg<128, 4, 32, 3, 2>; };
+template <> struct Choice<128> { using C = Cfg<128, 4, 32, 2, 2>; };
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* cu,
                     const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
-                    void* out, hipStream_t stream) {
+                    void* out, hipStream_t stream, hipEvent_t e0,
+                    hipEvent_t e1) {
   using C = typename Choice<D>::C;
   static_assert(C::BM == bf16_block_m_const(D), "work-list block size mismatch");
-  return launch_cfg<C>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
+  return launch_cfg<C>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const int32_t* cu,
                             const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                            float scale, void* out, hipStream_t stream) {
+                            float scale, void* out, hipStream_t stream, hipEvent_t e0,
+                            hipEvent_t e1) {
   switch (D) {
-    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
-    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
-    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
-    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
-    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
+    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
+    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
+    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
+    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
+    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

@@ -11,6 +11,7 @@
 // accumulator, and the two partial dot products are joined with one lane
 // exchange, so both lanes see bit-identical scores.  Keys stream through LDS in
 // tiles of 32 rows with a per-key online softmax.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -112,11 +113,12 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* cu,
                     const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
-                    void* out, hipStream_t stream) {
+                    void* out, hipStream_t stream, hipEvent_t e0,
+                    hipEvent_t e1) {
   const int64_t units = cap * int64_t(H);
   if (units <= 0) return hipSuccess;
   const int64_t grid = units < kMaxAttnGrid ? units : kMaxAttnGrid;
-  hipLaunchKernelGGL(attn_f32_kernel<D>, dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+  hipExtLaunchKernelGGL(attn_f32_kernel<D>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, e0, e1, 0,
                      static_cast<const float*>(q), static_cast<const float*>(k),
                      static_cast<const float*>(v), cu, items, meta, H, scale,
                      static_cast<float*>(out));
@@ -127,13 +129,14 @@ hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* 
 
 hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu,
                            const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                           float scale, void* out, hipStream_t stream) {
+                           float scale, void* out, hipStream_t stream, hipEvent_t e0,
+                            hipEvent_t e1) {
   switch (D) {
-    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
-    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
-    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
-    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
-    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, stream);
+    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
+    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
+    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
+    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
+    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

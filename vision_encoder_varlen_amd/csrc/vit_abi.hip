@@ -20,6 +20,27 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Events that the next attention launch on this thread records at its
+// kernel's dispatch start and end (set by vit_time_next_attention).
+struct TimingHook {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+thread_local TimingHook g_timing;
+
+TimingHook take_timing() {
+  const TimingHook t = g_timing;
+  g_timing = TimingHook{};
+  return t;
+}
+
+// A call that launches no kernel still records the hook's events, back to back.
+hipError_t record_empty(const TimingHook& t, hipStream_t stream) {
+  if (!t.start) return hipSuccess;
+  hipError_t e = hipEventRecord(t.start, stream);
+  return e == hipSuccess ? hipEventRecord(t.stop, stream) : e;
+}
+
 int fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -109,12 +130,16 @@ int block_m_for(int dtype, int D) {
 int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, int num_seqs,
                 int max_seqlen, int H, int D, float scale, void* out, hipStream_t stream,
                 int dtype) {
+  const TimingHook t = take_timing();
   int rc = check_attn_args(q, k, v, cu, num_seqs, max_seqlen, H, D, scale, out);
   if (rc != VIT_OK) return rc;
   if (int64_t(max_seqlen) * H * D * 2 > vit::kMaxSegmentBytes)
     return fail(VIT_ERR_UNSUPPORTED, "max_seqlen * num_heads * head_dim * 2 bytes exceeds %lld",
                 (long long)vit::kMaxSegmentBytes);
-  if (num_seqs == 0 || max_seqlen == 0) return ok();
+  if (num_seqs == 0 || max_seqlen == 0) {
+    const hipError_t e = record_empty(t, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
+  }
   const int bm = block_m_for(dtype, D);
   const int64_t cap = capacity(num_seqs, max_seqlen, bm);
   if (cap > kMaxCapacity) return fail(VIT_ERR_UNSUPPORTED, "work-list capacity %lld too large", (long long)cap);
@@ -126,8 +151,8 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, 
   hipError_t e = vit::launch_worklist(cu, num_seqs, max_seqlen, bm, items, cap, meta, stream);
   if (e != hipSuccess) return hip_fail(e, "work-list launch");
   e = dtype == VIT_BF16
-          ? vit::launch_attn_bf16(q, k, v, cu, items, cap, meta, H, D, scale, out, stream)
-          : vit::launch_attn_f32(q, k, v, cu, items, cap, meta, H, D, scale, out, stream);
+          ? vit::launch_attn_bf16(q, k, v, cu, items, cap, meta, H, D, scale, out, stream, t.start, t.stop)
+          : vit::launch_attn_f32(q, k, v, cu, items, cap, meta, H, D, scale, out, stream, t.start, t.stop);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
 }
@@ -218,15 +243,21 @@ int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
                             const int32_t* cu_seqlens, const int32_t* items, int64_t cap,
                             const int32_t* meta, int num_heads, int head_dim, float scale,
                             int dtype, void* out, hipStream_t stream) {
+  const TimingHook t = take_timing();
   if (!items || !meta) return fail(VIT_ERR_INVALID_ARG, "null work-list pointer");
   if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   int rc = check_attn_args(q, k, v, cu_seqlens, 0, 0, num_heads, head_dim, scale, out);
   if (rc != VIT_OK) return rc;
   if (cap < 0 || cap > kMaxCapacity) return fail(VIT_ERR_INVALID_ARG, "bad work-list capacity %lld", (long long)cap);
-  if (cap == 0) return ok();
+  if (cap == 0) {
+    const hipError_t e = record_empty(t, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
+  }
   hipError_t e = dtype == VIT_BF16
-      ? vit::launch_attn_bf16(q, k, v, cu_seqlens, items, cap, meta, num_heads, head_dim, scale, out, stream)
-      : vit::launch_attn_f32(q, k, v, cu_seqlens, items, cap, meta, num_heads, head_dim, scale, out, stream);
+      ? vit::launch_attn_bf16(q, k, v, cu_seqlens, items, cap, meta, num_heads, head_dim, scale,
+                              out, stream, t.start, t.stop)
+      : vit::launch_attn_f32(q, k, v, cu_seqlens, items, cap, meta, num_heads, head_dim, scale,
+                             out, stream, t.start, t.stop);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
 }
@@ -249,6 +280,13 @@ int vit_device_error(hipStream_t stream, int32_t* err, int reset) {
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail(e, "clearing the work-list error word");
   }
+  return ok();
+}
+
+int vit_time_next_attention(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(VIT_ERR_INVALID_ARG, "start and stop must both be events or both be null");
+  g_timing = TimingHook{start, stop};
   return ok();
 }
 

@@ -37,12 +37,16 @@ hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
 hipError_t launch_worklist(const int32_t* cu, int N, int max_seqlen, int block_m,
                            int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream);
 
+// Attention launches: ev_start / ev_stop (both null, or both timing events)
+// are recorded at the kernel's dispatch start and end (hipExtLaunchKernel).
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const int32_t* cu,
                             const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                            float scale, void* out, hipStream_t stream);
+                            float scale, void* out, hipStream_t stream, hipEvent_t ev_start,
+                            hipEvent_t ev_stop);
 
 hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu,
                            const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                           float scale, void* out, hipStream_t stream);
+                           float scale, void* out, hipStream_t stream, hipEvent_t ev_start,
+                           hipEvent_t ev_stop);
 
 }  // namespace vit

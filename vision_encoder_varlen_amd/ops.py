@@ -183,3 +183,16 @@ def device_error(reset: bool = False, device: Optional[torch.device] = None) -> 
 
 def release() -> None:
     _lib.load().vit_release()
+
+
+def time_next_attention(start: Optional["torch.cuda.Event"], stop: Optional["torch.cuda.Event"]) -> None:
+    """Have the next attention call on this thread record ``start``/``stop`` at
+    its kernel's dispatch start and end (events need ``enable_timing=True``).
+    ``None, None`` clears the hook."""
+    if start is None and stop is None:
+        _lib.check(_lib.load().vit_time_next_attention(None, None))
+        return
+    for ev in (start, stop):
+        if ev.cuda_event == 0:     # torch creates the HIP event on first record
+            ev.record()
+    _lib.check(_lib.load().vit_time_next_attention(start.cuda_event, stop.cuda_event))

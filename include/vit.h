@@ -174,17 +174,19 @@ const char* vit_last_error(void);
 
 /*
  * Timing hook for profilers and benchmarks.  The next call on this host thread
- * of vit_varlen_attn, vit_varlen_attn_f32 or vit_varlen_attn_planned records
- * `start` when its attention kernel's dispatch begins and `stop` when it ends
- * (hipExtLaunchKernel's dispatch timestamps: the kernel alone, without launch
- * gaps); the hook is then cleared, whether that call succeeds or not.  A call
- * that launches no kernel records both events back to back on its stream.
- * The work-list launch made inside vit_varlen_attn* is not timed.
+ * of vit_qk_norm_rope, vit_varlen_worklist, vit_varlen_attn_planned,
+ * vit_varlen_attn or vit_varlen_attn_f32 records `start` when its kernel's
+ * dispatch begins and `stop` when that kernel ends (hipExtLaunchKernel's
+ * dispatch timestamps: the kernel alone, without launch gaps); the hook is
+ * then cleared, whether that call succeeds or not.  For vit_varlen_attn and
+ * vit_varlen_attn_f32 the timed kernel is the attention kernel, not the
+ * work-list build they launch first.  A call that launches no kernel records
+ * both events back to back on its stream.
  *  start, stop: events created with timing enabled, owned by the caller, or
  *               both null to clear the hook.
  * Returns VIT_ERR_INVALID_ARG when exactly one of them is null.
  */
-int vit_time_next_attention(hipEvent_t start, hipEvent_t stop);
+int vit_time_next_kernel(hipEvent_t start, hipEvent_t stop);
 
 /* Frees all library-owned scratch on every device (synchronises each device first). */
 void vit_release(void);

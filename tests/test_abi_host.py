@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
     for required in ("vit_qk_norm_rope", "vit_varlen_attn", "vit_varlen_attn_f32",
                      "vit_varlen_worklist", "vit_varlen_attn_planned", "vit_attn_block_m",
                      "vit_worklist_capacity", "vit_device_error", "vit_last_error", "vit_release",
-                     "vit_time_next_attention"):
+                     "vit_time_next_kernel"):
         assert required in names
     assert sorted(_lib.SIGNATURES) == names
 
@@ -137,7 +137,7 @@ def test_error_message_is_thread_local(lib):
 
 
 def test_timing_hook_needs_both_events_or_neither(lib):
-    assert lib.vit_time_next_attention(FAKE, None) == _lib.VIT_ERR_INVALID_ARG
+    assert lib.vit_time_next_kernel(FAKE, None) == _lib.VIT_ERR_INVALID_ARG
     assert "both" in _err(lib)
-    assert lib.vit_time_next_attention(None, FAKE) == _lib.VIT_ERR_INVALID_ARG
-    assert lib.vit_time_next_attention(None, None) == _lib.VIT_OK
+    assert lib.vit_time_next_kernel(None, FAKE) == _lib.VIT_ERR_INVALID_ARG
+    assert lib.vit_time_next_kernel(None, None) == _lib.VIT_OK

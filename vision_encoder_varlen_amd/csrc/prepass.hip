@@ -20,6 +20,7 @@
 //     log2(G)-step xor shuffle inside the lane group).  Loads and stores are 8
 //     bytes (bf16) or 16 bytes (fp32) per lane per half row, and every row is
 //     read and written exactly once.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -166,7 +167,8 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
 
 hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
                           const int32_t* pos, const double* inv_freq_host, const float* wq,
-                          const float* wk, float eps, hipStream_t stream) {
+                          const float* wk, float eps, hipStream_t stream, hipEvent_t e0,
+                          hipEvent_t e1) {
   if (T <= 0 || (pos == nullptr && wq == nullptr)) return hipSuccess;
   int G = 1;
   while (G * 8 < D) G <<= 1;                 // lanes per (token, head) row
@@ -188,11 +190,11 @@ hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
   const long long grid = groups < 65536 ? groups : 65536;
   const size_t lds = pos != nullptr ? size_t(tok_per_grp) * (D / 2) * sizeof(float) * 2 : 0;
   if (dtype == 1) {
-    hipLaunchKernelGGL(prepass_kernel<u16>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
+    hipExtLaunchKernelGGL(prepass_kernel<u16>, dim3(unsigned(grid)), dim3(kThreads), lds, stream, e0, e1, 0,
                        static_cast<u16*>(q), static_cast<u16*>(k), (long long)T, H, D, G,
                        tok_per_grp, pos, fr, wq, wk, eps);
   } else {
-    hipLaunchKernelGGL(prepass_kernel<float>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
+    hipExtLaunchKernelGGL(prepass_kernel<float>, dim3(unsigned(grid)), dim3(kThreads), lds, stream, e0, e1, 0,
                        static_cast<float*>(q), static_cast<float*>(k), (long long)T, H, D, G,
                        tok_per_grp, pos, fr, wq, wk, eps);
   }

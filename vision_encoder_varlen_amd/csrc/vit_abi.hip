@@ -20,8 +20,8 @@ namespace {
 
 thread_local std::string g_last_error;
 
-// Events that the next attention launch on this thread records at its
-// kernel's dispatch start and end (set by vit_time_next_attention).
+// Events that the next kernel-launching call on this thread records at its
+// kernel's dispatch start and end (set by vit_time_next_kernel).
 struct TimingHook {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
@@ -148,7 +148,8 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, 
   if (rc != VIT_OK) return rc;
   int32_t* meta = s->buf;
   int32_t* items = s->buf + 4;
-  hipError_t e = vit::launch_worklist(cu, num_seqs, max_seqlen, bm, items, cap, meta, stream);
+  hipError_t e = vit::launch_worklist(cu, num_seqs, max_seqlen, bm, items, cap, meta, stream,
+                                      nullptr, nullptr);
   if (e != hipSuccess) return hip_fail(e, "work-list launch");
   e = dtype == VIT_BF16
           ? vit::launch_attn_bf16(q, k, v, cu, items, cap, meta, H, D, scale, out, stream, t.start, t.stop)
@@ -164,6 +165,7 @@ extern "C" {
 int vit_qk_norm_rope(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
                      int dtype, const int32_t* pos, float theta, const float* q_weight,
                      const float* k_weight, float eps, hipStream_t stream) {
+  const TimingHook t = take_timing();
   if (!q || !k) return fail(VIT_ERR_INVALID_ARG, "null q or k");
   if (total_tokens < 0) return fail(VIT_ERR_INVALID_ARG, "total_tokens must be >= 0");
   if (num_heads < 1) return fail(VIT_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", num_heads);
@@ -181,13 +183,16 @@ int vit_qk_norm_rope(void* q, void* k, int64_t total_tokens, int num_heads, int 
     return fail(VIT_ERR_INVALID_ARG, "norm weights must be 16-byte aligned");
   if (pos && !aligned4(pos)) return fail(VIT_ERR_INVALID_ARG, "pos must be 4-byte aligned");
   if (q == k) return fail(VIT_ERR_INVALID_ARG, "q and k must be distinct buffers");
-  if (total_tokens == 0 || (pos == nullptr && q_weight == nullptr)) return ok();
+  if (total_tokens == 0 || (pos == nullptr && q_weight == nullptr)) {
+    const hipError_t e = record_empty(t, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
+  }
   // Rotary inverse frequencies for dim = D/2: theta^(-2j/(D/2)), in double.
   double inv_freq[64];
   const int F = head_dim / 4;
   for (int j = 0; j < F; ++j) inv_freq[j] = std::pow(double(theta), -2.0 * j / (head_dim / 2.0));
   hipError_t e = vit::launch_prepass(q, k, total_tokens, num_heads, head_dim, dtype, pos,
-                                     inv_freq, q_weight, k_weight, eps, stream);
+                                     inv_freq, q_weight, k_weight, eps, stream, t.start, t.stop);
   if (e != hipSuccess) return hip_fail(e, "pre-pass launch");
   return ok();
 }
@@ -221,6 +226,7 @@ int64_t vit_worklist_capacity(int num_seqs, int max_seqlen, int block_m) {
 
 int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int block_m,
                         int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream) {
+  const TimingHook t = take_timing();
   if (!cu_seqlens || !items || !meta) return fail(VIT_ERR_INVALID_ARG, "null pointer argument");
   if (num_seqs < 0 || max_seqlen < 0) return fail(VIT_ERR_INVALID_ARG, "negative size");
   if (num_seqs > vit::kWorklistMaxSeqs)
@@ -234,7 +240,8 @@ int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
                 (long long)need);
   if (!aligned4(cu_seqlens) || !aligned4(items) || !aligned4(meta))
     return fail(VIT_ERR_INVALID_ARG, "int32 buffers must be 4-byte aligned");
-  hipError_t e = vit::launch_worklist(cu_seqlens, num_seqs, max_seqlen, block_m, items, cap, meta, stream);
+  hipError_t e = vit::launch_worklist(cu_seqlens, num_seqs, max_seqlen, block_m, items, cap, meta,
+                                      stream, t.start, t.stop);
   if (e != hipSuccess) return hip_fail(e, "work-list launch");
   return ok();
 }
@@ -283,7 +290,7 @@ int vit_device_error(hipStream_t stream, int32_t* err, int reset) {
   return ok();
 }
 
-int vit_time_next_attention(hipEvent_t start, hipEvent_t stop) {
+int vit_time_next_kernel(hipEvent_t start, hipEvent_t stop) {
   if ((start == nullptr) != (stop == nullptr))
     return fail(VIT_ERR_INVALID_ARG, "start and stop must both be events or both be null");
   g_timing = TimingHook{start, stop};

@@ -7,6 +7,9 @@
 
 namespace vit {
 
+// Every launch_* takes ev_start / ev_stop: both null, or both timing events
+// that are recorded at its kernel's dispatch start and end (hipExtLaunchKernel).
+
 // Query rows per (segment, q-tile) work item.
 // bf16 MFMA kernel: 4 waves x 32 rows.
 constexpr int bf16_block_m_const(int /*head_dim*/) { return 128; }
@@ -32,13 +35,13 @@ inline bool attn_head_dim_supported(int D) {
 // (may be null when pos is null).  dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
                           const int32_t* pos, const double* inv_freq_host,
-                          const float* wq, const float* wk, float eps, hipStream_t stream);
+                          const float* wq, const float* wk, float eps, hipStream_t stream,
+                          hipEvent_t ev_start, hipEvent_t ev_stop);
 
 hipError_t launch_worklist(const int32_t* cu, int N, int max_seqlen, int block_m,
-                           int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream);
+                           int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream,
+                           hipEvent_t ev_start, hipEvent_t ev_stop);
 
-// Attention launches: ev_start / ev_stop (both null, or both timing events)
-// are recorded at the kernel's dispatch start and end (hipExtLaunchKernel).
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const int32_t* cu,
                             const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
                             float scale, void* out, hipStream_t stream, hipEvent_t ev_start,

@@ -17,6 +17,7 @@
 // the order above; a sortedness check skips the bitonic network when the input
 // is already ordered (uniform batches, single images); an exclusive scan of the
 // per-segment tile counts gives each segment its slice of the list.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -142,7 +143,8 @@ __global__ __launch_bounds__(kThreads) void worklist_kernel(
 }  // namespace
 
 hipError_t launch_worklist(const int32_t* cu, int N, int max_seqlen, int block_m,
-                           int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream) {
+                           int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream,
+                           hipEvent_t e0, hipEvent_t e1) {
   int npad = 1;
   while (npad < N) npad <<= 1;
   const size_t lds = size_t(npad) * (sizeof(unsigned long long) + sizeof(int));
@@ -151,7 +153,7 @@ hipError_t launch_worklist(const int32_t* cu, int N, int max_seqlen, int block_m
                                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kThreads), lds, stream, cu, N, npad,
+  hipExtLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kThreads), lds, stream, e0, e1, 0, cu, N, npad,
                      max_seqlen, block_m, items, static_cast<long long>(cap), meta);
   return hipGetLastError();
 }

@@ -185,14 +185,15 @@ def release() -> None:
     _lib.load().vit_release()
 
 
-def time_next_attention(start: Optional["torch.cuda.Event"], stop: Optional["torch.cuda.Event"]) -> None:
-    """Have the next attention call on this thread record ``start``/``stop`` at
-    its kernel's dispatch start and end (events need ``enable_timing=True``).
+def time_next_kernel(start: Optional["torch.cuda.Event"], stop: Optional["torch.cuda.Event"]) -> None:
+    """Have the next kernel-launching call of this module on this thread record
+    ``start``/``stop`` at its kernel's dispatch start and end (for the attention
+    calls: the attention kernel).  Events need ``enable_timing=True``;
     ``None, None`` clears the hook."""
     if start is None and stop is None:
-        _lib.check(_lib.load().vit_time_next_attention(None, None))
+        _lib.check(_lib.load().vit_time_next_kernel(None, None))
         return
     for ev in (start, stop):
         if ev.cuda_event == 0:     # torch creates the HIP event on first record
             ev.record()
-    _lib.check(_lib.load().vit_time_next_attention(start.cuda_event, stop.cuda_event))
+    _lib.check(_lib.load().vit_time_next_kernel(start.cuda_event, stop.cuda_event))

@@ -28,10 +28,11 @@
 //  * V stays row-major in LDS; the A operand of O^T = V^T P^T (eight
 //    consecutive keys of one head-dim column per lane) comes from two
 //    ds_read_b64_tr_b16 transpose reads.
-//  * LDS row strides, in 16-byte units: K rows use an odd count (eight rows
-//    read at the same column by ds_read_b128 hit distinct banks); V rows use
-//    2 mod 8 (the four rows x 32 bytes a transpose-read lane group touches hit
-//    distinct banks).
+//  * LDS row strides, in 16-byte units (the LDS has 64 four-byte banks, 256
+//    bytes per clock): K rows use an odd count (the sixteen rows a
+//    ds_read_b128 serves together, read at the same column, hit distinct
+//    banks); V rows use 4 mod 8 (a ds_read_b64_tr_b16 serves 32 lanes
+//    together, four rows x 64 bytes, which then hit distinct banks).
 //  * Softmax in base 2: p = 2^(s*c - m) with c = scale*log2(e), one FMA and
 //    one v_exp_f32 per score.  The reference max m is only raised (and O, l
 //    rescaled) when a tile's max exceeds it by more than kRescaleSlack, so
@@ -66,7 +67,7 @@ constexpr unsigned kPadOffset = 0x40000000u;
 static_assert(kMaxSegmentBytes <= (int64_t)kPadOffset, "pad offset must exceed every segment");
 
 constexpr int odd_units(int u) { return (u & 1) ? u : u + 1; }
-constexpr int units_2_mod_8(int u) { return u + ((2 - u % 8) + 8) % 8; }
+constexpr int units_4_mod_8(int u) { return u % 8 == 4 ? u : units_4_mod_8(u + 1); }
 
 template <int D_, int WAVES_, int BN_, int STAGES_, int OCC_>
 struct Cfg {
@@ -82,7 +83,7 @@ struct Cfg {
   static constexpr int DB = (D + 31) / 32;              // 32-row blocks of O^T
   static constexpr int DU = D / 8;                      // 16-byte units per row of data
   static constexpr int KSTR = odd_units(DU);            // K row stride (units)
-  static constexpr int VSTR = units_2_mod_8(DU);        // V row stride (units)
+  static constexpr int VSTR = units_4_mod_8(DU);        // V row stride (units)
   static constexpr int NK = (BN * KSTR + 63) / 64;      // copy instructions for K
   static constexpr int NV = (BN * VSTR + 63) / 64;      // copy instructions for V
   static constexpr int NT = NK + NV;                    // copy instructions per tile

@@ -94,7 +94,16 @@ def test_large_scores_stay_stable():
     x.q = x.q * 8.0   # exact in bf16; logits of order 100
     got, _ = _gpu_attn(x, wl)
     want = oracle.varlen_attention(x.q, x.k, x.v, x.cu_seqlens, wl.softmax_scale)
-    assert_attn_close(got, want, "bf16", "peaked softmax")
+    # Peaked rows return nearly single V rows, some of magnitude 4..8.  There
+    # the bf16 weights P (relative rounding 2^-9, as the reference itself
+    # rounds P to the input dtype) and the bf16 store of the result (another
+    # 2^-9) move an output by up to 2^-8 of its magnitude, which exceeds
+    # 1.5e-2 once |out| > 3.8; the bound adds that relative term.
+    err = np.abs(got - want)
+    tol = 1.5e-2 + 2.0 ** -8 * np.abs(want)
+    assert np.all(np.isfinite(got))
+    assert np.all(err <= tol), f"peaked softmax: worst {float((err / tol).max()):.3f} of the bound"
+    assert np.linalg.norm(got - want) / np.linalg.norm(want) <= 5e-3
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -183,9 +192,9 @@ def test_errors_raise_value_error():
 
 @pytest.mark.parametrize("D", [80, 128])
 def test_logit_jump_after_first_tile(D):
-    """Keys after the first tile score far above every key of the first tile
-    (a jump of several hundred logits), so the kernel's running reference max
-    must move after it was first used."""
+    """Keys after the first key tile score far above every key of that tile
+    (a jump of several hundred logits), so a reference max taken from the first
+    tile must be replaced after it was first used."""
     rng = np.random.default_rng(13)
     lens = [300, 97]
     wl = W.from_seqlens(lens, H=2, D=D, dtype="bf16", seed=13)
@@ -196,9 +205,12 @@ def test_logit_jump_after_first_tile(D):
     big = 4.0 * np.sqrt(D)                      # |q| = |k| = 4 sqrt(D): logits ~ +-16 D * scale
     q = np.broadcast_to(big * u, (sum(lens), 2, D)).copy()
     k = x.k.copy() * 0.01
-    k[:40] -= big * u                          # first tile of each head: strongly negative
-    k[300:310] -= big * u
-    k[60:] += big * u * (rng.random((sum(lens) - 60, 1, 1)) > 0.5)
+    k[:64] -= big * u                          # first 64 keys of each segment: strongly negative
+    k[300:364] -= big * u
+    jump = rng.random((sum(lens), 1, 1)) > 0.5
+    jump[:64] = False
+    jump[300:364] = False
+    k += big * u * jump                        # about half of the later keys: strongly positive
     x.q = q.astype(np.float32)
     x.k = k.astype(np.float32)
     from vision_encoder_varlen_amd.workloads import bf16_bits_to_f32, f32_to_bf16_bits

@@ -7,8 +7,9 @@
 // cu_seqlens_q = cu_seqlens_k).  The S x S mask of VisionAttention.forward is
 // never formed: each workgroup only visits its own segment's keys.
 //
-// Design (one workgroup = WAVES waves; each wave owns 32 query rows of one
-// head; two workgroups share a CU so one's softmax overlaps the other's MFMA):
+// Design (one workgroup = WAVES waves; each wave owns 32*QB query rows of
+// one head; two workgroups share a CU so one's softmax overlaps the other's
+// MFMA):
 //  * Q fragments stay in VGPRs for the whole key loop.
 //  * K and V tiles of BN keys are copied global -> LDS by the buffer unit
 //    itself (buffer_load_dwordx4 ... lds) into a ring of STAGES buffers, issued
@@ -33,10 +34,16 @@
 //    ds_read_b128 serves together, read at the same column, hit distinct
 //    banks); V rows use 4 mod 8 (a ds_read_b64_tr_b16 serves 32 lanes
 //    together, four rows x 64 bytes, which then hit distinct banks).
-//  * Softmax in base 2: p = 2^(s*c - m) with c = scale*log2(e), one FMA and
-//    one v_exp_f32 per score.  The reference max m is only raised (and O, l
-//    rescaled) when a tile's max exceeds it by more than kRescaleSlack, so
-//    p <= 2^kRescaleSlack and the rescale is skipped for almost every tile.
+//  * Softmax in base 2: p = 2^(s*c - m_ref) with c = scale*log2(e), one FMA
+//    and one v_exp_f32 per score.  The reference max m_ref of a query row is
+//    fixed for a whole pass over the keys (taken from the first key tile), so
+//    O is never rescaled and the key loop touches the accumulators only
+//    through MFMAs.  A tile whose max exceeds m_ref by more than
+//    kRestartSlack makes the workgroup repeat the unit with m_ref set to the
+//    row max seen over all keys; every p is then <= 2^kRestartSlack and the
+//    fp32 sums cannot overflow.
+//  * QB > 1 gives a wave several 32-row query blocks, so each K and V
+//    fragment read from LDS feeds QB MFMAs.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -59,7 +66,7 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) const u16 lds_u16_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleSlack = 8.0f;     // log2 units: p stays <= 256
+constexpr float kRestartSlack = 64.0f;    // log2 units: p stays <= 2^64
 constexpr int kRsrcWord3 = 0x00020000;    // gfx9-family buffer descriptor word 3 (raw, 32-bit)
 // Byte offset for copy lanes that fill padding: past any segment's num_records
 // (segments are limited to kMaxSegmentBytes) even after adding the tile offset.
@@ -69,15 +76,16 @@ static_assert(kMaxSegmentBytes <= (int64_t)kPadOffset, "pad offset must exceed e
 constexpr int odd_units(int u) { return (u & 1) ? u : u + 1; }
 constexpr int units_4_mod_8(int u) { return u % 8 == 4 ? u : units_4_mod_8(u + 1); }
 
-template <int D_, int WAVES_, int BN_, int STAGES_, int OCC_>
+template <int D_, int WAVES_, int QB_, int BN_, int STAGES_, int OCC_>
 struct Cfg {
   static constexpr int D = D_;
   static constexpr int WAVES = WAVES_;
+  static constexpr int QB = QB_;                        // 32-row query blocks per wave
   static constexpr int BN = BN_;                        // keys per tile
   static constexpr int STAGES = STAGES_;                // LDS ring depth
   static constexpr int OCC = OCC_;                      // waves per SIMD the kernel is built for
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int BM = 32 * WAVES;                 // query rows per workgroup
+  static constexpr int BM = 32 * QB * WAVES;            // query rows per workgroup
   static constexpr int KB = BN / 32;                    // 32-key blocks per tile
   static constexpr int KSTEPS = D / 16;                 // 16-wide contraction steps of Q K^T
   static constexpr int DB = (D + 31) / 32;              // 32-row blocks of O^T
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
     const int32_t* __restrict__ meta, int H, float scale_log2, u16* __restrict__ out) {
-  constexpr int D = C::D, BN = C::BN, KB = C::KB, STAGES = C::STAGES, NI = C::NI_HI;
+  constexpr int D = C::D, BN = C::BN, KB = C::KB, STAGES = C::STAGES, NI = C::NI_HI, QB = C::QB;
   __shared__ __align__(16) u16 smem[C::LDS_BYTES / 2];
 
   const int tid = threadIdx.x;
@@ -213,37 +221,41 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     // Offsets are 32-bit: a segment larger than the addressable span is skipped
     // (the host rejects the max_seqlen that would allow it).
     if (int64_t(len) * tok_stride * 2 > kMaxSegmentBytes) continue;
-    const int row0 = qt * C::BM + wave * 32;  // first query row of this wave
+    const int row0 = qt * C::BM + wave * 32 * QB;  // first query row of this wave
     const bool wave_active = row0 < len;
     const unsigned seg_bytes = unsigned(((len - 1) * tok_stride + D) * 2);
     const i32x4_t krs = make_rsrc(k + size_t(start) * tok_stride + size_t(h) * D, seg_bytes);
     const i32x4_t vrs = make_rsrc(v + size_t(start) * tok_stride + size_t(h) * D, seg_bytes);
 
-    // Q^T fragments (B operand of S^T = K Q^T): lane holds 8 dims of its row.
-    bf16x8_t qf[C::KSTEPS];
-    {
-      const int row = row0 + l32;
+    // Q^T fragments (B operand of S^T = K Q^T): lane holds 8 dims of its row
+    // in each of the wave's QB query blocks.
+    bf16x8_t qf[QB][C::KSTEPS];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int row = row0 + 32 * b + l32;
       if (row < len) {
         const u16* qp = q + size_t(start + row) * tok_stride + size_t(h) * D + half * 8;
 #pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s)
-          qf[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qp + s * 16));
+        for (int st = 0; st < C::KSTEPS; ++st)
+          qf[b][st] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qp + st * 16));
       } else {
 #pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s) qf[s] = bf16x8_t{};
+        for (int st = 0; st < C::KSTEPS; ++st) qf[b][st] = bf16x8_t{};
       }
     }
-    f32x16_t o[C::DB];
+
+    // Reference max per query row (log2 domain), fixed for a whole pass over
+    // the keys: p = 2^(s*c - m_ref) needs no rescaling of O, so the key loop
+    // never touches the accumulators outside the MFMAs.  The first pass takes
+    // m_ref from the first key tile; if a later tile exceeds it by more than
+    // kRestartSlack, the pass is discarded and repeated with m_ref = the row
+    // max that pass saw over all keys, so every p <= 2^kRestartSlack and the
+    // fp32 sums cannot overflow.
+    float m_ref[QB], m_seen[QB];
 #pragma unroll
-    for (int d = 0; d < C::DB; ++d) o[d] = f32x16_t{};
-    float m_run = -INFINITY;  // reference max, log2 domain
-    float l_run = 0.f;        // this lane's partial row sum
-
-    // Nothing of ours may be in flight when the copy pipeline starts counting,
-    // and the previous unit's last tile must no longer be read.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
+    for (int b = 0; b < QB; ++b) m_ref[b] = m_seen[b] = -INFINITY;
+    f32x16_t o[QB][C::DB];
+    float l_run[QB];
     const int ntiles = (len + BN - 1) / BN;
     auto issue_tile = [&](int t) {
       const unsigned tile_off = unsigned(t) * unsigned(BN * 2) * unsigned(tok_stride);
@@ -253,22 +265,37 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
         if (j < C::NI_LO || wave_hi)
           copy_to_lds(stage_lds + cp_lds[j], cp_off[j] + tile_off, cp_is_k[j] ? krs : vrs);
     };
+
+    for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int t = 0; t < STAGES - 1; ++t)
-      if (t < ntiles) issue_tile(t);
+      for (int b = 0; b < QB; ++b) {
+#pragma unroll
+        for (int d = 0; d < C::DB; ++d) o[b][d] = f32x16_t{};
+        l_run[b] = 0.f;  // this lane's partial row sum
+      }
+      bool restart = false;
 
-    // One key tile.  MASKED is true only for the last, partial tile.
-    auto process_tile = [&](auto masked_tag, int t) {
-      constexpr bool MASKED = decltype(masked_tag)::value;
-      // Own copies of tile t done: at most min(STAGES-2, ntiles-1-t) later
-      // tiles' copies may still be in flight.
-      const int later = min(ntiles - 1 - t, STAGES - 2);
-      if (wave_hi) wait_copies<C::NI_HI, STAGES>(later);
-      else wait_copies<C::NI_LO, STAGES>(later);
-      __syncthreads();  // everyone's copies of tile t landed; tile t-1 is free
-      if (t + STAGES - 1 < ntiles) issue_tile(t + STAGES - 1);
+      // Nothing of ours may be in flight when the copy pipeline starts
+      // counting, and the previous unit's (or pass's) last tile must no
+      // longer be read.
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < STAGES - 1; ++t)
+        if (t < ntiles) issue_tile(t);
 
-      if (wave_active) {
+      // One key tile.  MASKED is true only for the last, partial tile.
+      auto process_tile = [&](auto masked_tag, int t) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        // Own copies of tile t done: at most min(STAGES-2, ntiles-1-t) later
+        // tiles' copies may still be in flight.
+        const int later = min(ntiles - 1 - t, STAGES - 2);
+        if (wave_hi) wait_copies<C::NI_HI, STAGES>(later);
+        else wait_copies<C::NI_LO, STAGES>(later);
+        __syncthreads();  // everyone's copies of tile t landed; tile t-1 is free
+        if (t + STAGES - 1 < ntiles) issue_tile(t + STAGES - 1);
+        if (!wave_active) return;
+
         const int kv0 = t * BN;
         const u16* stage = smem + (t % STAGES) * C::STAGE_UNITS * 8;
         // All LDS fragment reads of the tile are issued up front, K first, so
@@ -303,79 +330,85 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
             }
         __builtin_amdgcn_sched_barrier(0);
 
-        // S^T = K Q^T.
-        f32x16_t s[KB];
+        // S^T = K Q^T for every query block (each K fragment feeds QB MFMAs).
+        f32x16_t sc[QB][KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          s[kb] = f32x16_t{};
+        for (int b = 0; b < QB; ++b)
 #pragma unroll
-          for (int st = 0; st < C::KSTEPS; ++st)
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][st], qf[st], s[kb], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+          for (int kb = 0; kb < KB; ++kb) {
+            sc[b][kb] = f32x16_t{};
+#pragma unroll
+            for (int st = 0; st < C::KSTEPS; ++st)
+              sc[b][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][st], qf[b][st], sc[b][kb], 0, 0, 0);
+          }
 
-        // Online softmax.  Register r of block kb holds key
-        // kv0 + 32kb + 16(r>>3) + 8half + (r&7) for query row l32.
-        bf16x8_t p[KB][2];
-        float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int b = 0; b < QB; ++b) {
+          // Softmax of block b.  Register r of block kb holds key
+          // kv0 + 32kb + 16(r>>3) + 8half + (r&7) for query row l32.
+          float mx = -INFINITY;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = POS_SCALE ? s[kb][r] : s[kb][r] * scale_log2;
-            if constexpr (MASKED) {
-              const int key = kv0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
-              if (key >= len) x = -INFINITY;
+          for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              float x = POS_SCALE ? sc[b][kb][r] : sc[b][kb][r] * scale_log2;
+              if constexpr (MASKED) {
+                const int key = kv0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
+                if (key >= len) x = -INFINITY;
+              }
+              sc[b][kb][r] = x;
+              mx = fmaxf(mx, x);
             }
-            s[kb][r] = x;
-            mx = fmaxf(mx, x);
           }
-        }
-        mx = fmaxf(mx, other_half(mx));
-        const float mt = POS_SCALE ? mx * scale_log2 : mx;  // tile max, log2 domain
-        if (__any(mt > m_run + kRescaleSlack)) {
-          const float m_new = fmaxf(m_run, mt);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-          m_run = m_new;
-          l_run *= alpha;
+          mx = fmaxf(mx, other_half(mx));
+          const float mt = POS_SCALE ? mx * scale_log2 : mx;  // tile max, log2 domain
+          m_seen[b] = fmaxf(m_seen[b], mt);
+          if (t == 0 && pass == 0) m_ref[b] = mt;
+          restart |= mt > m_ref[b] + kRestartSlack;
+          const float neg_m = -m_ref[b];
+          bf16x8_t p[KB][2];
+          float part[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
 #pragma unroll
-          for (int d = 0; d < C::DB; ++d) o[d] *= alpha;
-        }
-        const float neg_m = -m_run;
-        float part[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
+          for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = POS_SCALE ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, neg_m))
-                                      : __builtin_amdgcn_exp2f(s[kb][r] + neg_m);
-            part[r & 3] += e;
-            p[kb][r >> 3][r & 7] = (__bf16)e;
+            for (int r = 0; r < 16; ++r) {
+              const float e = POS_SCALE ? __builtin_amdgcn_exp2f(fmaf(sc[b][kb][r], scale_log2, neg_m))
+                                        : __builtin_amdgcn_exp2f(sc[b][kb][r] + neg_m);
+              part[r & 3] += e;
+              p[kb][r >> 3][r & 7] = (__bf16)e;
+            }
           }
+          l_run[b] += (part[0] + part[1]) + (part[2] + part[3]);
+
+          // O^T += V^T P^T (each V fragment feeds QB MFMAs).
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+              for (int d = 0; d < C::DB; ++d)
+                o[b][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8_t, vf[kb][s2][d]), p[kb][s2], o[b][d], 0, 0, 0);
         }
-        l_run += (part[0] + part[1]) + (part[2] + part[3]);
-        __builtin_amdgcn_sched_barrier(0);
+      };
 
-        // O^T += V^T P^T.
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int d = 0; d < C::DB; ++d)
-              o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8_t, vf[kb][s2][d]), p[kb][s2], o[d], 0, 0, 0);
-      }
-    };
+      const int nfull = len / BN;
+      for (int t = 0; t < nfull; ++t) process_tile(std::false_type{}, t);
+      if (nfull < ntiles) process_tile(std::true_type{}, nfull);
 
-    const int nfull = len / BN;
-    for (int t = 0; t < nfull; ++t) process_tile(std::false_type{}, t);
-    if (nfull < ntiles) process_tile(std::true_type{}, nfull);
+      // Every wave shares the copy ring, so the workgroup repeats or ends
+      // the pass together.  The second pass uses the exact row max, so it
+      // never asks for a third.
+      if (!__syncthreads_or(restart)) break;
+#pragma unroll
+      for (int b = 0; b < QB; ++b) m_ref[b] = m_seen[b];
+    }
 
     // Finalize: O^T register r of block d holds dim 32d + 8(r>>2) + 4half + (r&3).
-    {
-      const int row = row0 + l32;
-      const float l_tot = l_run + other_half(l_run);
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int row = row0 + 32 * b + l32;
+      const float l_tot = l_run[b] + other_half(l_run[b]);
       if (row < len) {
         const float inv = 1.f / l_tot;
         u16* op = out + size_t(start + row) * tok_stride + size_t(h) * D;
@@ -387,7 +420,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
             if (d0 < D) {
               __bf16 w[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[d][4 * g + e] * inv);
+              for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[b][d][4 * g + e] * inv);
               *reinterpret_cast<u32x2_t*>(op + d0) = __builtin_bit_cast(u32x2_t, w);
             }
           }
@@ -416,11 +449,11 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const int32_t
 // Per head dim: (waves, keys per tile, ring depth, waves per SIMD).  Rows per
 // workgroup must equal bf16_block_m_const(D).
 template <int D> struct Choice;
-template <> struct Choice<32> { using C = Cfg<32, 4, 32, 3, 2>; };
-template <> struct Choice<64> { using C = Cfg<64, 4, 32, 3, 2>; };
-template <> struct Choice<80> { using C = Cfg<80, 4, 64, 2, 2>; };
-template <> struct Choice<96> { using C = Cfg<96, 4, 32, 4, 2>; };
-template <> struct Choice<128> { using C = Cfg<128, 4, 32, 2, 2>; };
+template <> struct Choice<32> { using C = Cfg<32, 4, 1, 32, 3, 2>; };
+template <> struct Choice<64> { using C = Cfg<64, 4, 1, 32, 3, 2>; };
+template <> struct Choice<80> { using C = Cfg<80, 4, 1, 64, 2, 2>; };
+template <> struct Choice<96> { using C = Cfg<96, 4, 1, 32, 4, 2>; };
+template <> struct Choice<128> { using C = Cfg<128, 4, 1, 32, 2, 2>; };
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* cu,

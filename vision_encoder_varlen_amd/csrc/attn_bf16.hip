@@ -177,6 +177,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
     const int32_t* __restrict__ meta, int H, float scale_log2, u16* __restrict__ out) {
   constexpr int D = C::D, BN = C::BN, KB = C::KB, STAGES = C::STAGES, NI = C::NI_HI, QB = C::QB;
+  // When D is not a multiple of 32 the last 32-row block of O^T has padding
+  // rows; row D then collects the row sums of P (see the tile loop), and
+  // lane kOnesLane (l&31) of that block is the one that reads it.
+  constexpr bool kSumByMfma = C::DB * 32 > D;
+  constexpr int kOnesLane = D - 32 * (C::DB - 1);
   __shared__ __align__(16) u16 smem[C::LDS_BYTES / 2];
 
   const int tid = threadIdx.x;
@@ -284,9 +289,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       for (int t = 0; t < STAGES - 1; ++t)
         if (t < ntiles) issue_tile(t);
 
-      // One key tile.  MASKED is true only for the last, partial tile.
-      auto process_tile = [&](auto masked_tag, int t) {
+      // One key tile.  MASKED: the partial last tile.  FIRST: tile 0, whose
+      // max sets the reference on the first pass.
+      auto process_tile = [&](auto masked_tag, auto first_tag, int t) {
         constexpr bool MASKED = decltype(masked_tag)::value;
+        constexpr bool FIRST = decltype(first_tag)::value;
         // Own copies of tile t done: at most min(STAGES-2, ntiles-1-t) later
         // tiles' copies may still be in flight.
         const int later = min(ntiles - 1 - t, STAGES - 2);
@@ -329,6 +336,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
               vf[kb][s2][d][1] = ds_read_tr16(base + 4 * C::VSTR * 8);
             }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kSumByMfma) {
+          // Head-dim row D of V^T (padding, zero in LDS) becomes all ones, so
+          // row D of O^T accumulates the row sums of P.
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+              for (int qh = 0; qh < 2; ++qh)
+                if (l32 == kOnesLane) vf[kb][s2][C::DB - 1][qh] = i16x4_t{0x3f80, 0x3f80, 0x3f80, 0x3f80};
+        }
 
         // S^T = K Q^T for every query block (each K fragment feeds QB MFMAs).
         f32x16_t sc[QB][KB];
@@ -342,10 +360,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
               sc[b][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][st], qf[b][st], sc[b][kb], 0, 0, 0);
           }
 
+        // Softmax.  Register r of block kb holds key
+        // kv0 + 32kb + 16(r>>3) + 8half + (r&7) for query row l32.  The
+        // exponentials of a 32-key block need only m_ref, so (after the first
+        // tile) block kb's exponentials and P V products overlap the MFMAs of
+        // the neighbouring blocks; the tile max only feeds the repeat check.
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
-          // Softmax of block b.  Register r of block kb holds key
-          // kv0 + 32kb + 16(r>>3) + 8half + (r&7) for query row l32.
           float mx = -INFINITY;
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
@@ -363,38 +384,43 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
           mx = fmaxf(mx, other_half(mx));
           const float mt = POS_SCALE ? mx * scale_log2 : mx;  // tile max, log2 domain
           m_seen[b] = fmaxf(m_seen[b], mt);
-          if (t == 0 && pass == 0) m_ref[b] = mt;
+          if constexpr (FIRST) {
+            if (pass == 0) m_ref[b] = mt;
+          }
           restart |= mt > m_ref[b] + kRestartSlack;
           const float neg_m = -m_ref[b];
-          bf16x8_t p[KB][2];
-          float part[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
+            bf16x8_t p[2];
+            float part[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const float e = POS_SCALE ? __builtin_amdgcn_exp2f(fmaf(sc[b][kb][r], scale_log2, neg_m))
                                         : __builtin_amdgcn_exp2f(sc[b][kb][r] + neg_m);
-              part[r & 3] += e;
-              p[kb][r >> 3][r & 7] = (__bf16)e;
+              if constexpr (!kSumByMfma) part[r & 3] += e;
+              p[r >> 3][r & 7] = (__bf16)e;
             }
-          }
-          l_run[b] += (part[0] + part[1]) + (part[2] + part[3]);
+            if constexpr (!kSumByMfma) l_run[b] += (part[0] + part[1]) + (part[2] + part[3]);
 
-          // O^T += V^T P^T (each V fragment feeds QB MFMAs).
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
+            // O^T += V^T P^T (each V fragment feeds QB MFMAs).
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
               for (int d = 0; d < C::DB; ++d)
                 o[b][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8_t, vf[kb][s2][d]), p[kb][s2], o[b][d], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8_t, vf[kb][s2][d]), p[s2], o[b][d], 0, 0, 0);
+          }
         }
       };
 
       const int nfull = len / BN;
-      for (int t = 0; t < nfull; ++t) process_tile(std::false_type{}, t);
-      if (nfull < ntiles) process_tile(std::true_type{}, nfull);
+      if (nfull == 0) {
+        process_tile(std::true_type{}, std::true_type{}, 0);
+      } else {
+        process_tile(std::false_type{}, std::true_type{}, 0);
+        for (int t = 1; t < nfull; ++t) process_tile(std::false_type{}, std::false_type{}, t);
+        if (nfull < ntiles) process_tile(std::true_type{}, std::false_type{}, nfull);
+      }
 
       // Every wave shares the copy ring, so the workgroup repeats or ends
       // the pass together.  The second pass uses the exact row max, so it
@@ -408,7 +434,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
       const int row = row0 + 32 * b + l32;
-      const float l_tot = l_run[b] + other_half(l_run[b]);
+      float l_tot;
+      if constexpr (kSumByMfma) {
+        // O^T register r of block DB-1 holds dim 32(DB-1) + 8(r>>2) + 4half + (r&3).
+        constexpr int rr = kOnesLane;  // offset of dim D inside the last block
+        constexpr int r = 4 * (rr >> 3) + (rr & 3);
+        const float v = o[b][C::DB - 1][r];
+        const float w = other_half(v);
+        l_tot = ((rr >> 2) & 1) == 0 ? (half == 0 ? v : w) : (half == 1 ? v : w);
+      } else {
+        l_tot = l_run[b] + other_half(l_run[b]);
+      }
       if (row < len) {
         const float inv = 1.f / l_tot;
         u16* op = out + size_t(start + row) * tok_stride + size_t(h) * D;

@@ -19,7 +19,10 @@
 //     rotation is lane-local and only the sum of squares crosses lanes (a
 //     log2(G)-step xor shuffle inside the lane group).  Loads and stores are 8
 //     bytes (bf16) or 16 bytes (fp32) per lane per half row, and every row is
-//     read and written exactly once.
+//     read and written exactly once.  A lane issues the four loads of its row
+//     (q and k, both halves) before any arithmetic, and token groups are small
+//     (about two rows per lane), so many workgroups keep enough loads in
+//     flight to approach the HBM bandwidth.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -85,6 +88,14 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
   const bool lane_active = m0 < half_d;
   const int rows_per_pass = kThreads / G;
   const int rows_per_grp = tok_per_grp * H;
+  // Norm weights of this lane's dims, the same for every row.
+  float wa[2][4] = {}, wb[2][4] = {};
+  if (norm && lane_active) {
+    load4(wq + m0, wa[0]);
+    load4(wq + m0 + half_d, wb[0]);
+    load4(wk + m0, wa[1]);
+    load4(wk + m0 + half_d, wb[1]);
+  }
 
   for (long long t0 = (long long)blockIdx.x * tok_per_grp; t0 < T_tok;
        t0 += (long long)gridDim.x * tok_per_grp) {
@@ -115,47 +126,57 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
       const int tl = row / H;
       const int h = row - tl * H;
       const size_t base = (size_t(t0 + tl) * H + h) * size_t(D);
+      // Both tensors' loads are issued before any arithmetic, so each lane
+      // keeps four independent loads in flight.
+      float a[2][4] = {}, b[2][4] = {};
+      if (row_ok) {
+        load4(q + base + m0, a[0]);
+        load4(q + base + m0 + half_d, b[0]);
+        load4(k + base + m0, a[1]);
+        load4(k + base + m0 + half_d, b[1]);
+      }
+      if (norm) {
+        float ss[2];
 #pragma unroll
-      for (int which = 0; which < 2; ++which) {
-        T* const x_ptr = which == 0 ? q : k;
-        const float* const w = which == 0 ? wq : wk;
-        float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
-        if (row_ok) {
-          load4(x_ptr + base + m0, a);
-          load4(x_ptr + base + m0 + half_d, b);
+        for (int which = 0; which < 2; ++which) {
+          ss[which] = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            ss[which] = fmaf(a[which][e], a[which][e], fmaf(b[which][e], b[which][e], ss[which]));
         }
-        if (norm) {
-          float ss = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ss = fmaf(a[e], a[e], fmaf(b[e], b[e], ss));
-          for (int off = G >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-          const float rinv = rsqrtf(ss * inv_d + eps);
-          if (row_ok) {
-            float wa[4], wb[4];
-            load4(w + m0, wa);
-            load4(w + m0 + half_d, wb);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              a[e] = a[e] * rinv * wa[e];
-              b[e] = b[e] * rinv * wb[e];
-            }
-          }
+        for (int off = G >> 1; off > 0; off >>= 1) {
+          ss[0] += __shfl_xor(ss[0], off);
+          ss[1] += __shfl_xor(ss[1], off);
         }
-        if (rope && row_ok) {
-          const float2* c = cs + tl * half_d + m0;
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+          const float rinv = rsqrtf(ss[which] * inv_d + eps);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float2 cse = c[e];
-            const float ya = a[e] * cse.x - b[e] * cse.y;
-            const float yb = b[e] * cse.x + a[e] * cse.y;
-            a[e] = ya;
-            b[e] = yb;
+            a[which][e] = a[which][e] * rinv * wa[which][e];
+            b[which][e] = b[which][e] * rinv * wb[which][e];
           }
         }
-        if (row_ok) {
-          store4(x_ptr + base + m0, a);
-          store4(x_ptr + base + m0 + half_d, b);
+      }
+      if (rope && row_ok) {
+        const float2* c = cs + tl * half_d + m0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float2 cse = c[e];
+#pragma unroll
+          for (int which = 0; which < 2; ++which) {
+            const float ya = a[which][e] * cse.x - b[which][e] * cse.y;
+            const float yb = b[which][e] * cse.x + a[which][e] * cse.y;
+            a[which][e] = ya;
+            b[which][e] = yb;
+          }
         }
+      }
+      if (row_ok) {
+        store4(q + base + m0, a[0]);
+        store4(q + base + m0 + half_d, b[0]);
+        store4(k + base + m0, a[1]);
+        store4(k + base + m0 + half_d, b[1]);
       }
     }
     (void)rows_per_grp;
@@ -173,9 +194,9 @@ hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
   int G = 1;
   while (G * 8 < D) G <<= 1;                 // lanes per (token, head) row
   const int rows_per_pass = kThreads / G;
-  // About eight rows per lane per token group keeps loads in flight while the
-  // cos/sin table stays small.
-  int tok_per_grp = (8 * rows_per_pass) / H;
+  // About two rows per lane per token group: many small workgroups keep the
+  // most loads in flight, and the cos/sin table is still shared by all heads.
+  int tok_per_grp = (2 * rows_per_pass) / H;
   if (tok_per_grp < 1) tok_per_grp = 1;
   const int max_tok_lds = 32768 / (D / 2 * int(sizeof(float) * 2));
   if (tok_per_grp > max_tok_lds) tok_per_grp = max_tok_lds;

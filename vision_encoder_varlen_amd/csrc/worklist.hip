@@ -12,11 +12,13 @@
 // Attention workgroups are dispatched in list order, so the longest segments'
 // tiles start first and the short ones fill the tail.
 //
-// One workgroup of 1024 threads does everything in LDS, with no host sync:
+// One workgroup (one wave for up to 64 segments, up to 1024 threads for
+// 8192) does everything in LDS, with no host sync:
 // keys (len, index) are packed into 64-bit words so an ascending sort gives
 // the order above; a sortedness check skips the bitonic network when the input
 // is already ordered (uniform batches, single images); an exclusive scan of the
-// per-segment tile counts gives each segment its slice of the list.
+// per-segment tile counts (shuffles inside each wave, then the wave totals)
+// gives each segment its slice of the list.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -26,35 +28,56 @@
 namespace vit {
 namespace {
 
-constexpr int kThreads = 1024;
 constexpr unsigned long long kEmpty = ~0ull;
 
-__global__ __launch_bounds__(kThreads) void worklist_kernel(
+// Exclusive prefix over the workgroup of one int per thread, plus the total:
+// a shuffle scan inside each wave, then the wave totals through LDS (one
+// barrier).
+template <int THREADS>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < THREADS / 64; ++w) {
+    const int t = s_wave[w];
+    before += w < wave ? t : 0;
+    all += t;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void worklist_kernel(
     const int32_t* __restrict__ cu, int N, int npad, int max_seqlen, int block_m,
     int32_t* __restrict__ items, long long cap, int32_t* __restrict__ meta) {
   extern __shared__ __align__(16) unsigned long long keys[];  // [npad]
   int* const offs = reinterpret_cast<int*>(keys + npad);       // [npad] exclusive tile offsets
-  __shared__ int s_err;
-  __shared__ int s_unsorted;
-  __shared__ int s_partial[kThreads];
+  __shared__ int s_wave[THREADS / 64];
 
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    s_err = (N > 0 && cu[0] != 0) ? 1 : 0;
-    s_unsorted = 0;
-  }
-  __syncthreads();
-  const bool cu0_bad = s_err & 1;
+  // Every thread reads cu[0] with its own entries: one round trip to memory.
+  const bool cu0_bad = N > 0 && cu[0] != 0;
+  int err = cu0_bad ? 1 : 0;
 
   // 1. keys: high word = 0x7fffffff - len (ascending = longest first), low = index.
-  for (int i = tid; i < npad; i += kThreads) {
+  for (int i = tid; i < npad; i += THREADS) {
     unsigned long long key = kEmpty;
     if (i < N && !cu0_bad) {
       const int len = cu[i + 1] - cu[i];
       if (len < 0) {
-        atomicOr(&s_err, 2);
+        err |= 2;
       } else if (len > max_seqlen) {
-        atomicOr(&s_err, 4);
+        err |= 4;
       } else if (len > 0) {
         key = (static_cast<unsigned long long>(0x7fffffffu - static_cast<unsigned>(len)) << 32) |
               static_cast<unsigned>(i);
@@ -62,16 +85,17 @@ __global__ __launch_bounds__(kThreads) void worklist_kernel(
     }
     keys[i] = key;
   }
-  __syncthreads();
+  const int err_any = __syncthreads_or(err & 2) ? 2 : 0;
+  const int err_long = __syncthreads_or(err & 4) ? 4 : 0;
 
   // 2. sort only when needed.
-  for (int i = tid; i + 1 < npad; i += kThreads)
-    if (keys[i] > keys[i + 1]) s_unsorted = 1;
-  __syncthreads();
-  if (s_unsorted) {
+  int unsorted = 0;
+  for (int i = tid; i + 1 < npad; i += THREADS)
+    if (keys[i] > keys[i + 1]) unsorted = 1;
+  if (__syncthreads_or(unsorted)) {
     for (int size = 2; size <= npad; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < npad; i += kThreads) {
+        for (int i = tid; i < npad; i += THREADS) {
           const int j = i ^ stride;
           if (j > i) {
             const unsigned long long a = keys[i], b = keys[j];
@@ -88,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void worklist_kernel(
   }
 
   // 3. exclusive scan of tile counts: each thread owns a contiguous chunk.
-  const int chunk = (npad + kThreads - 1) / kThreads;
+  const int chunk = (npad + THREADS - 1) / THREADS;
   const int c0 = tid * chunk;
   int local = 0;
   for (int i = c0; i < c0 + chunk && i < npad; ++i) {
@@ -101,27 +125,18 @@ __global__ __launch_bounds__(kThreads) void worklist_kernel(
     offs[i] = nt;
     local += nt;
   }
-  s_partial[tid] = local;
-  __syncthreads();
-  for (int d = 1; d < kThreads; d <<= 1) {  // inclusive Hillis-Steele scan of partials
-    const int add = tid >= d ? s_partial[tid - d] : 0;
-    __syncthreads();
-    s_partial[tid] += add;
-    __syncthreads();
-  }
-  int run = s_partial[tid] - local;  // exclusive prefix of this chunk
+  int total = 0;
+  int run = block_exclusive_scan<THREADS>(local, s_wave, &total);
   for (int i = c0; i < c0 + chunk && i < npad; ++i) {
     const int nt = offs[i];
     offs[i] = run;
     run += nt;
   }
-  const int total = s_partial[kThreads - 1];
-  __syncthreads();
 
-  // 4. scatter.
+  // 4. scatter (each thread reads back only the offsets it wrote).
   const bool overflow = static_cast<long long>(total) > cap;
   if (!overflow) {
-    for (int i = tid; i < npad; i += kThreads) {
+    for (int i = c0; i < c0 + chunk && i < npad; ++i) {
       const unsigned long long key = keys[i];
       if (key == kEmpty) continue;
       const int seg = int(key & 0xffffffffu);
@@ -136,8 +151,23 @@ __global__ __launch_bounds__(kThreads) void worklist_kernel(
   }
   if (tid == 0) {
     meta[0] = overflow ? 0 : total;
-    meta[1] = s_err | (overflow ? 8 : 0);
+    meta[1] = (cu0_bad ? 1 : 0) | err_any | err_long | (overflow ? 8 : 0);
   }
+}
+
+template <int THREADS>
+hipError_t launch_t(const int32_t* cu, int N, int npad, int max_seqlen, int block_m,
+                    int32_t* items, long long cap, int32_t* meta, hipStream_t stream,
+                    hipEvent_t e0, hipEvent_t e1) {
+  const size_t lds = size_t(npad) * (sizeof(unsigned long long) + sizeof(int));
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(worklist_kernel<THREADS>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipExtLaunchKernelGGL(worklist_kernel<THREADS>, dim3(1), dim3(THREADS), lds, stream, e0, e1, 0,
+                        cu, N, npad, max_seqlen, block_m, items, cap, meta);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -147,15 +177,11 @@ hipError_t launch_worklist(const int32_t* cu, int N, int max_seqlen, int block_m
                            hipEvent_t e0, hipEvent_t e1) {
   int npad = 1;
   while (npad < N) npad <<= 1;
-  const size_t lds = size_t(npad) * (sizeof(unsigned long long) + sizeof(int));
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(worklist_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
-  }
-  hipExtLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kThreads), lds, stream, e0, e1, 0, cu, N, npad,
-                     max_seqlen, block_m, items, static_cast<long long>(cap), meta);
-  return hipGetLastError();
+  // One wave for small batches (no cross-wave barriers on the critical path),
+  // up to 1024 threads for large ones.
+  if (npad <= 64) return launch_t<64>(cu, N, npad, max_seqlen, block_m, items, cap, meta, stream, e0, e1);
+  if (npad <= 1024) return launch_t<256>(cu, N, npad, max_seqlen, block_m, items, cap, meta, stream, e0, e1);
+  return launch_t<1024>(cu, N, npad, max_seqlen, block_m, items, cap, meta, stream, e0, e1);
 }
 
 }  // namespace vit

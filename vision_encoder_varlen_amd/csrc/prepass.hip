@@ -14,15 +14,15 @@
 //     evaluated once per token rather than once per head and tensor (accurate
 //     sincosf; the inverse frequencies arrive precomputed in the kernel
 //     arguments);
-//  2. each (token, head) row is handled by G = next_pow2(D/8) consecutive lanes;
-//     a lane owns dims m..m+3 and their rotary partners m+D/2..m+D/2+3, so the
-//     rotation is lane-local and only the sum of squares crosses lanes (a
-//     log2(G)-step xor shuffle inside the lane group).  Loads and stores are 8
-//     bytes (bf16) or 16 bytes (fp32) per lane per half row, and every row is
-//     read and written exactly once.  A lane issues the four loads of its row
-//     (q and k, both halves) before any arithmetic, and token groups are small
-//     (about two rows per lane), so many workgroups keep enough loads in
-//     flight to approach the HBM bandwidth.
+//  2. each (token, head) row is handled by G consecutive lanes of a wave; a
+//     lane owns E consecutive dims m..m+E-1 of the first half and their rotary
+//     partners m+D/2.., so the rotation is lane-local and only the sum of
+//     squares crosses lanes (an xor shuffle when G is a power of two).  E = 8
+//     for bf16 rows (16-byte accesses; a D = 80 row takes 5 lanes, so a wave
+//     holds 12 rows), else 4.  Every row is read and written exactly once.  A
+//     lane issues the four loads of its row (q and k, both halves) before any
+//     arithmetic, and token groups are small (about two rows per lane), so
+//     many workgroups keep enough loads in flight to approach HBM bandwidth.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -51,26 +51,56 @@ __device__ __forceinline__ float bf16_to_f32(unsigned int bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-__device__ __forceinline__ void load4(const float* p, float x[4]) {
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// E consecutive elements <-> fp32 registers (one 8- or 16-byte access).
+template <int E>
+__device__ __forceinline__ void loadE(const float* p, float x[E]) {
+  static_assert(E == 4, "fp32 rows are handled 4 elements per access");
   const float4 v = *reinterpret_cast<const float4*>(p);
   x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
 }
-__device__ __forceinline__ void store4(float* p, const float x[4]) {
+template <int E>
+__device__ __forceinline__ void storeE(float* p, const float x[E]) {
+  static_assert(E == 4, "fp32 rows are handled 4 elements per access");
   *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
-__device__ __forceinline__ void load4(const u16* p, float x[4]) {
-  const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
-  x[0] = bf16_to_f32(v.x & 0xffffu); x[1] = bf16_to_f32(v.x >> 16);
-  x[2] = bf16_to_f32(v.y & 0xffffu); x[3] = bf16_to_f32(v.y >> 16);
-}
-__device__ __forceinline__ void store4(u16* p, const float x[4]) {
-  __bf16 w[4];
+template <int E>
+__device__ __forceinline__ void loadE(const u16* p, float x[E]) {
+  if constexpr (E == 8) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = (__bf16)x[e];  // round to nearest even
-  *reinterpret_cast<u32x2_t*>(p) = __builtin_bit_cast(u32x2_t, w);
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_to_f32(v[i] & 0xffffu);
+      x[2 * i + 1] = bf16_to_f32(v[i] >> 16);
+    }
+  } else {
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
+    x[0] = bf16_to_f32(v.x & 0xffffu); x[1] = bf16_to_f32(v.x >> 16);
+    x[2] = bf16_to_f32(v.y & 0xffffu); x[3] = bf16_to_f32(v.y >> 16);
+  }
+}
+template <int E>
+__device__ __forceinline__ void storeE(u16* p, const float x[E]) {
+  __bf16 w[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) w[e] = (__bf16)x[e];  // round to nearest even
+  if constexpr (E == 8) *reinterpret_cast<u32x4_t*>(p) = __builtin_bit_cast(u32x4_t, w);
+  else *reinterpret_cast<u32x2_t*>(p) = __builtin_bit_cast(u32x2_t, w);
 }
 
-template <typename T>
+// Sum of v over the G consecutive lanes [base, base + G) of a row.
+__device__ __forceinline__ float row_sum(float v, int G, int base) {
+  if ((G & (G - 1)) == 0) {
+    for (int off = G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+  }
+  float t = 0.f;
+  for (int j = 0; j < G; ++j) t += __shfl(v, base + j);
+  return t;
+}
+
+template <typename T, int E>
 __global__ __launch_bounds__(kThreads) void prepass_kernel(
     T* __restrict__ q, T* __restrict__ k, long long T_tok, int H, int D, int G, int tok_per_grp,
     const int32_t* __restrict__ pos, Freqs freqs, const float* __restrict__ wq,
@@ -83,18 +113,25 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
   const bool norm = wq != nullptr;
   const float inv_d = 1.f / float(D);
 
-  const int lane_g = tid & (G - 1);        // lane inside the row group
-  const int m0 = lane_g * 4;                // first dim of this lane (first half)
-  const bool lane_active = m0 < half_d;
-  const int rows_per_pass = kThreads / G;
-  const int rows_per_grp = tok_per_grp * H;
+  // A row takes G consecutive lanes of a wave; a wave holds 64 / G rows.
+  const int lane = tid & 63;
+  const int rows_per_wave = 64 / G;
+  const int rw = lane / G;
+  const int lane_g = lane - rw * G;       // lane inside the row
+  const int m0 = lane_g * E;              // first dim of this lane (first half)
+  const bool lane_active = rw < rows_per_wave;
+  const int rows_per_pass = (kThreads / 64) * rows_per_wave;
+  const int row_in_pass = (tid >> 6) * rows_per_wave + rw;
   // Norm weights of this lane's dims, the same for every row.
-  float wa[2][4] = {}, wb[2][4] = {};
+  float wa[2][E] = {}, wb[2][E] = {};
   if (norm && lane_active) {
-    load4(wq + m0, wa[0]);
-    load4(wq + m0 + half_d, wb[0]);
-    load4(wk + m0, wa[1]);
-    load4(wk + m0 + half_d, wb[1]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      wa[0][e] = wq[m0 + e];
+      wb[0][e] = wq[m0 + half_d + e];
+      wa[1][e] = wk[m0 + e];
+      wb[1][e] = wk[m0 + half_d + e];
+    }
   }
 
   for (long long t0 = (long long)blockIdx.x * tok_per_grp; t0 < T_tok;
@@ -111,29 +148,29 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
         // the rounding error of coord * hi.
         const float a_hi = coord * freqs.hi[j];
         const float a_lo = fmaf(coord, freqs.hi[j], -a_hi) + coord * freqs.lo[j];
-        float s, c;
-        sincosf(a_hi, &s, &c);
+        float sn, cn;
+        sincosf(a_hi, &sn, &cn);
         // first-order correction for a_lo (|a_lo| <= 2^-23 |a_hi|; the neglected
         // second-order term is below 2^-46 |a_hi|^2)
-        cs[i] = make_float2(fmaf(-s, a_lo, c), fmaf(c, a_lo, s));
+        cs[i] = make_float2(fmaf(-sn, a_lo, cn), fmaf(cn, a_lo, sn));
       }
       __syncthreads();
     }
 
     for (int r0 = 0; r0 < ntok * H; r0 += rows_per_pass) {
-      const int row = r0 + tid / G;  // (token_local, head) row inside the group
+      const int row = r0 + row_in_pass;  // (token_local, head) row inside the group
       const bool row_ok = row < ntok * H && lane_active;
       const int tl = row / H;
       const int h = row - tl * H;
       const size_t base = (size_t(t0 + tl) * H + h) * size_t(D);
       // Both tensors' loads are issued before any arithmetic, so each lane
       // keeps four independent loads in flight.
-      float a[2][4] = {}, b[2][4] = {};
+      float a[2][E] = {}, b[2][E] = {};
       if (row_ok) {
-        load4(q + base + m0, a[0]);
-        load4(q + base + m0 + half_d, b[0]);
-        load4(k + base + m0, a[1]);
-        load4(k + base + m0 + half_d, b[1]);
+        loadE<E>(q + base + m0, a[0]);
+        loadE<E>(q + base + m0 + half_d, b[0]);
+        loadE<E>(k + base + m0, a[1]);
+        loadE<E>(k + base + m0 + half_d, b[1]);
       }
       if (norm) {
         float ss[2];
@@ -141,18 +178,15 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
         for (int which = 0; which < 2; ++which) {
           ss[which] = 0.f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
+          for (int e = 0; e < E; ++e)
             ss[which] = fmaf(a[which][e], a[which][e], fmaf(b[which][e], b[which][e], ss[which]));
-        }
-        for (int off = G >> 1; off > 0; off >>= 1) {
-          ss[0] += __shfl_xor(ss[0], off);
-          ss[1] += __shfl_xor(ss[1], off);
+          ss[which] = row_sum(ss[which], G, rw * G);
         }
 #pragma unroll
         for (int which = 0; which < 2; ++which) {
           const float rinv = rsqrtf(ss[which] * inv_d + eps);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int e = 0; e < E; ++e) {
             a[which][e] = a[which][e] * rinv * wa[which][e];
             b[which][e] = b[which][e] * rinv * wb[which][e];
           }
@@ -161,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
       if (rope && row_ok) {
         const float2* c = cs + tl * half_d + m0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < E; ++e) {
           const float2 cse = c[e];
 #pragma unroll
           for (int which = 0; which < 2; ++which) {
@@ -173,13 +207,12 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
         }
       }
       if (row_ok) {
-        store4(q + base + m0, a[0]);
-        store4(q + base + m0 + half_d, b[0]);
-        store4(k + base + m0, a[1]);
-        store4(k + base + m0 + half_d, b[1]);
+        storeE<E>(q + base + m0, a[0]);
+        storeE<E>(q + base + m0 + half_d, b[0]);
+        storeE<E>(k + base + m0, a[1]);
+        storeE<E>(k + base + m0 + half_d, b[1]);
       }
     }
-    (void)rows_per_grp;
     if (rope) __syncthreads();  // cs is rewritten by the next token group
   }
 }
@@ -191,9 +224,11 @@ hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
                           const float* wk, float eps, hipStream_t stream, hipEvent_t e0,
                           hipEvent_t e1) {
   if (T <= 0 || (pos == nullptr && wq == nullptr)) return hipSuccess;
-  int G = 1;
-  while (G * 8 < D) G <<= 1;                 // lanes per (token, head) row
-  const int rows_per_pass = kThreads / G;
+  // Elements per lane per half row: 8 (one 16-byte access) for bf16 rows
+  // whose half is a multiple of 8, else 4.  G lanes cover a row.
+  const int E = (dtype == 1 && (D / 2) % 8 == 0) ? 8 : 4;
+  const int G = (D / 2) / E;
+  const int rows_per_pass = (kThreads / 64) * (64 / G);
   // About two rows per lane per token group: many small workgroups keep the
   // most loads in flight, and the cos/sin table is still shared by all heads.
   int tok_per_grp = (2 * rows_per_pass) / H;
@@ -210,14 +245,18 @@ hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
   const long long groups = (T + tok_per_grp - 1) / tok_per_grp;
   const long long grid = groups < 65536 ? groups : 65536;
   const size_t lds = pos != nullptr ? size_t(tok_per_grp) * (D / 2) * sizeof(float) * 2 : 0;
-  if (dtype == 1) {
-    hipExtLaunchKernelGGL(prepass_kernel<u16>, dim3(unsigned(grid)), dim3(kThreads), lds, stream, e0, e1, 0,
-                       static_cast<u16*>(q), static_cast<u16*>(k), (long long)T, H, D, G,
-                       tok_per_grp, pos, fr, wq, wk, eps);
+  if (dtype == 1 && E == 8) {
+    hipExtLaunchKernelGGL(prepass_kernel<u16, 8>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
+                          e0, e1, 0, static_cast<u16*>(q), static_cast<u16*>(k), (long long)T, H, D,
+                          G, tok_per_grp, pos, fr, wq, wk, eps);
+  } else if (dtype == 1) {
+    hipExtLaunchKernelGGL(prepass_kernel<u16, 4>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
+                          e0, e1, 0, static_cast<u16*>(q), static_cast<u16*>(k), (long long)T, H, D,
+                          G, tok_per_grp, pos, fr, wq, wk, eps);
   } else {
-    hipExtLaunchKernelGGL(prepass_kernel<float>, dim3(unsigned(grid)), dim3(kThreads), lds, stream, e0, e1, 0,
-                       static_cast<float*>(q), static_cast<float*>(k), (long long)T, H, D, G,
-                       tok_per_grp, pos, fr, wq, wk, eps);
+    hipExtLaunchKernelGGL(prepass_kernel<float, 4>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
+                          e0, e1, 0, static_cast<float*>(q), static_cast<float*>(k), (long long)T, H,
+                          D, G, tok_per_grp, pos, fr, wq, wk, eps);
   }
   return hipGetLastError();
 }

@@ -37,11 +37,12 @@
 //  * Softmax in base 2: p = 2^(s*c - m_ref) with c = scale*log2(e), one FMA
 //    and one v_exp_f32 per score.  The reference max m_ref of a query row is
 //    fixed for a whole pass over the keys (taken from the first key tile), so
-//    O is never rescaled and the key loop touches the accumulators only
-//    through MFMAs.  A tile whose max exceeds m_ref by more than
-//    kRestartSlack makes the workgroup repeat the unit with m_ref set to the
-//    row max seen over all keys; every p is then <= 2^kRestartSlack and the
-//    fp32 sums cannot overflow.
+//    O is never rescaled, the key loop touches the accumulators only through
+//    MFMAs, and after the first tile no row max is computed at all.  If a
+//    row's sum of p ends above 2^64 (some key scored far above the first
+//    tile), the workgroup runs a max-only pass and repeats the unit with the
+//    exact row max, where every p <= 1.  Below the limit no p or partial sum
+//    can overflow fp32.
 //  * QB > 1 gives a wave several 32-row query blocks, so each K and V
 //    fragment read from LDS feeds QB MFMAs.
 #include <hip/hip_ext.h>
@@ -66,7 +67,9 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) const u16 lds_u16_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRestartSlack = 64.0f;    // log2 units: p stays <= 2^64
+constexpr float kRestartLimit = 0x1p64f;  // a row sum above this triggers the exact-max repeat
+// Tile modes of the key loop.
+constexpr int kSetRef = 0, kPlain = 1, kMaxOnly = 2;
 constexpr int kRsrcWord3 = 0x00020000;    // gfx9-family buffer descriptor word 3 (raw, 32-bit)
 // Byte offset for copy lanes that fill padding: past any segment's num_records
 // (segments are limited to kMaxSegmentBytes) even after adding the tile offset.
@@ -251,11 +254,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
 
     // Reference max per query row (log2 domain), fixed for a whole pass over
     // the keys: p = 2^(s*c - m_ref) needs no rescaling of O, so the key loop
-    // never touches the accumulators outside the MFMAs.  The first pass takes
-    // m_ref from the first key tile; if a later tile exceeds it by more than
-    // kRestartSlack, the pass is discarded and repeated with m_ref = the row
-    // max that pass saw over all keys, so every p <= 2^kRestartSlack and the
-    // fp32 sums cannot overflow.
+    // never touches the accumulators outside the MFMAs, and after the first
+    // tile it needs no row max either.  Pass 0 takes m_ref from the first key
+    // tile.  A row whose sum of p then exceeds kRestartLimit = 2^64 (or is not
+    // finite) means some later key scored far above that tile; the workgroup
+    // then runs a max-only pass over the keys and repeats the unit with the
+    // exact row max, where every p <= 1.
     float m_ref[QB], m_seen[QB];
 #pragma unroll
     for (int b = 0; b < QB; ++b) m_ref[b] = m_seen[b] = -INFINITY;
@@ -270,61 +274,58 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
         if (j < C::NI_LO || wave_hi)
           copy_to_lds(stage_lds + cp_lds[j], cp_off[j] + tile_off, cp_is_k[j] ? krs : vrs);
     };
-
-    for (int pass = 0;; ++pass) {
-#pragma unroll
-      for (int b = 0; b < QB; ++b) {
-#pragma unroll
-        for (int d = 0; d < C::DB; ++d) o[b][d] = f32x16_t{};
-        l_run[b] = 0.f;  // this lane's partial row sum
+    // Sum of p over the whole row b (both lane halves).
+    auto row_total = [&](int b) {
+      if constexpr (kSumByMfma) {
+        // O^T register r of block DB-1 holds dim 32(DB-1) + 8(r>>2) + 4half + (r&3).
+        constexpr int rr = kOnesLane;  // offset of dim D inside the last block
+        constexpr int r = 4 * (rr >> 3) + (rr & 3);
+        const float v = o[b][C::DB - 1][r];
+        const float w = other_half(v);
+        return ((rr >> 2) & 1) == 0 ? (half == 0 ? v : w) : (half == 1 ? v : w);
+      } else {
+        return l_run[b] + other_half(l_run[b]);
       }
-      bool restart = false;
+    };
 
-      // Nothing of ours may be in flight when the copy pipeline starts
-      // counting, and the previous unit's (or pass's) last tile must no
-      // longer be read.
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-#pragma unroll
-      for (int t = 0; t < STAGES - 1; ++t)
-        if (t < ntiles) issue_tile(t);
+    // One key tile.  MASKED: the partial last tile.  MODE: kSetRef (tile 0
+    // of pass 0: its max becomes m_ref), kPlain (exponentials and P V only),
+    // kMaxOnly (scores and row max only).
+    auto process_tile = [&](auto masked_tag, auto mode_tag, int t) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      constexpr int MODE = decltype(mode_tag)::value;
+      // Own copies of tile t done: at most min(STAGES-2, ntiles-1-t) later
+      // tiles' copies may still be in flight.
+      const int later = min(ntiles - 1 - t, STAGES - 2);
+      if (wave_hi) wait_copies<C::NI_HI, STAGES>(later);
+      else wait_copies<C::NI_LO, STAGES>(later);
+      __syncthreads();  // everyone's copies of tile t landed; tile t-1 is free
+      if (t + STAGES - 1 < ntiles) issue_tile(t + STAGES - 1);
+      if (!wave_active) return;
 
-      // One key tile.  MASKED: the partial last tile.  FIRST: tile 0, whose
-      // max sets the reference on the first pass.
-      auto process_tile = [&](auto masked_tag, auto first_tag, int t) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
-        constexpr bool FIRST = decltype(first_tag)::value;
-        // Own copies of tile t done: at most min(STAGES-2, ntiles-1-t) later
-        // tiles' copies may still be in flight.
-        const int later = min(ntiles - 1 - t, STAGES - 2);
-        if (wave_hi) wait_copies<C::NI_HI, STAGES>(later);
-        else wait_copies<C::NI_LO, STAGES>(later);
-        __syncthreads();  // everyone's copies of tile t landed; tile t-1 is free
-        if (t + STAGES - 1 < ntiles) issue_tile(t + STAGES - 1);
-        if (!wave_active) return;
-
-        const int kv0 = t * BN;
-        const u16* stage = smem + (t % STAGES) * C::STAGE_UNITS * 8;
-        // All LDS fragment reads of the tile are issued up front, K first, so
-        // their latency is paid once and the V reads land during the scores
-        // and the softmax.
-        bf16x8_t kf[KB][C::KSTEPS];
-        const u16* kt = stage + l32 * C::KSTR * 8 + half * 8;
+      const int kv0 = t * BN;
+      const u16* stage = smem + (t % STAGES) * C::STAGE_UNITS * 8;
+      // All LDS fragment reads of the tile are issued up front, K first, so
+      // their latency is paid once and the V reads land during the scores
+      // and the softmax.
+      bf16x8_t kf[KB][C::KSTEPS];
+      const u16* kt = stage + l32 * C::KSTR * 8 + half * 8;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int st = 0; st < C::KSTEPS; ++st)
-            kf[kb][st] = __builtin_bit_cast(
-                bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + kb * 32 * C::KSTR * 8 + st * 16));
-        // Transpose-read lane l (group g = l>>4, j = l&15) addresses V row (key)
-        // kb*32 + 16*s2 + 8*half + 4*qh + (j>>2), dims 32d + 16*(g&1) +
-        // 4*(j&3) .. +3, and receives keys kb*32 + 16*s2 + 8*half + 4*qh + 0..3
-        // of dim 32d + (l&31).  One LDS-space base; the per-read offsets are
-        // constants the compiler folds into the instructions.
+        for (int st = 0; st < C::KSTEPS; ++st)
+          kf[kb][st] = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + kb * 32 * C::KSTR * 8 + st * 16));
+      // Transpose-read lane l (group g = l>>4, j = l&15) addresses V row (key)
+      // kb*32 + 16*s2 + 8*half + 4*qh + (j>>2), dims 32d + 16*(g&1) +
+      // 4*(j&3) .. +3, and receives keys kb*32 + 16*s2 + 8*half + 4*qh + 0..3
+      // of dim 32d + (l&31).  One LDS-space base; the per-read offsets are
+      // constants the compiler folds into the instructions.
+      i16x4_t vf[KB][2][C::DB][2];
+      if constexpr (MODE != kMaxOnly) {
         lds_u16_t* const vbase = (lds_u16_t*)(stage + C::KREG * 8) +
                                  (8 * half + ((lane & 15) >> 2)) * C::VSTR * 8 +
                                  16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        i16x4_t vf[KB][2][C::DB][2];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -335,41 +336,41 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
               vf[kb][s2][d][0] = ds_read_tr16(base);
               vf[kb][s2][d][1] = ds_read_tr16(base + 4 * C::VSTR * 8);
             }
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kSumByMfma) {
-          // Head-dim row D of V^T (padding, zero in LDS) becomes all ones, so
-          // row D of O^T accumulates the row sums of P.
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kSumByMfma && MODE != kMaxOnly) {
+        // Head-dim row D of V^T (padding, zero in LDS) becomes all ones, so
+        // row D of O^T accumulates the row sums of P.
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
+          for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-              for (int qh = 0; qh < 2; ++qh)
-                if (l32 == kOnesLane) vf[kb][s2][C::DB - 1][qh] = i16x4_t{0x3f80, 0x3f80, 0x3f80, 0x3f80};
+            for (int qh = 0; qh < 2; ++qh)
+              if (l32 == kOnesLane) vf[kb][s2][C::DB - 1][qh] = i16x4_t{0x3f80, 0x3f80, 0x3f80, 0x3f80};
+      }
+
+      // S^T = K Q^T for every query block (each K fragment feeds QB MFMAs).
+      f32x16_t sc[QB][KB];
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          sc[b][kb] = f32x16_t{};
+#pragma unroll
+          for (int st = 0; st < C::KSTEPS; ++st)
+            sc[b][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][st], qf[b][st], sc[b][kb], 0, 0, 0);
         }
 
-        // S^T = K Q^T for every query block (each K fragment feeds QB MFMAs).
-        f32x16_t sc[QB][KB];
+      // Softmax.  Register r of block kb holds key
+      // kv0 + 32kb + 16(r>>3) + 8half + (r&7) for query row l32.  Block kb's
+      // exponentials need only m_ref, so they and its P V products overlap
+      // the MFMAs of the neighbouring blocks.
 #pragma unroll
-        for (int b = 0; b < QB; ++b)
+      for (int b = 0; b < QB; ++b) {
+        if constexpr (MASKED || !POS_SCALE) {
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            sc[b][kb] = f32x16_t{};
-#pragma unroll
-            for (int st = 0; st < C::KSTEPS; ++st)
-              sc[b][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][st], qf[b][st], sc[b][kb], 0, 0, 0);
-          }
-
-        // Softmax.  Register r of block kb holds key
-        // kv0 + 32kb + 16(r>>3) + 8half + (r&7) for query row l32.  The
-        // exponentials of a 32-key block need only m_ref, so (after the first
-        // tile) block kb's exponentials and P V products overlap the MFMAs of
-        // the neighbouring blocks; the tile max only feeds the repeat check.
-#pragma unroll
-        for (int b = 0; b < QB; ++b) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
+          for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               float x = POS_SCALE ? sc[b][kb][r] : sc[b][kb][r] * scale_log2;
@@ -378,16 +379,20 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
                 if (key >= len) x = -INFINITY;
               }
               sc[b][kb][r] = x;
-              mx = fmaxf(mx, x);
             }
-          }
+        }
+        if constexpr (MODE != kPlain) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][kb][r]);
           mx = fmaxf(mx, other_half(mx));
           const float mt = POS_SCALE ? mx * scale_log2 : mx;  // tile max, log2 domain
-          m_seen[b] = fmaxf(m_seen[b], mt);
-          if constexpr (FIRST) {
-            if (pass == 0) m_ref[b] = mt;
-          }
-          restart |= mt > m_ref[b] + kRestartSlack;
+          if constexpr (MODE == kSetRef) m_ref[b] = mt;
+          if constexpr (MODE == kMaxOnly) m_seen[b] = fmaxf(m_seen[b], mt);
+        }
+        if constexpr (MODE != kMaxOnly) {
           const float neg_m = -m_ref[b];
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
@@ -411,40 +416,55 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
                     __builtin_bit_cast(bf16x8_t, vf[kb][s2][d]), p[s2], o[b][d], 0, 0, 0);
           }
         }
-      };
+      }
+    };
 
+    // One pass over the keys: tile 0 in mode M0, the others in mode M.
+    auto run_pass = [&](auto m0_tag, auto m_tag) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+#pragma unroll
+        for (int d = 0; d < C::DB; ++d) o[b][d] = f32x16_t{};
+        l_run[b] = 0.f;  // this lane's partial row sum
+      }
+      // Nothing of ours may be in flight when the copy pipeline starts
+      // counting, and the previous unit's (or pass's) last tile must no
+      // longer be read.
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < STAGES - 1; ++t)
+        if (t < ntiles) issue_tile(t);
       const int nfull = len / BN;
       if (nfull == 0) {
-        process_tile(std::true_type{}, std::true_type{}, 0);
+        process_tile(std::true_type{}, m0_tag, 0);
       } else {
-        process_tile(std::false_type{}, std::true_type{}, 0);
-        for (int t = 1; t < nfull; ++t) process_tile(std::false_type{}, std::false_type{}, t);
-        if (nfull < ntiles) process_tile(std::true_type{}, std::false_type{}, nfull);
+        process_tile(std::false_type{}, m0_tag, 0);
+        for (int t = 1; t < nfull; ++t) process_tile(std::false_type{}, m_tag, t);
+        if (nfull < ntiles) process_tile(std::true_type{}, m_tag, nfull);
       }
+    };
 
-      // Every wave shares the copy ring, so the workgroup repeats or ends
-      // the pass together.  The second pass uses the exact row max, so it
-      // never asks for a third.
-      if (!__syncthreads_or(restart)) break;
+    run_pass(std::integral_constant<int, kSetRef>{}, std::integral_constant<int, kPlain>{});
+    bool repeat = false;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const float lt = row_total(b);  // every lane takes part in the half exchange
+      repeat |= wave_active && row0 + 32 * b + l32 < len && !(lt <= kRestartLimit);
+    }
+    // Every wave shares the copy ring, so the workgroup repeats together.
+    if (__syncthreads_or(repeat)) {
+      run_pass(std::integral_constant<int, kMaxOnly>{}, std::integral_constant<int, kMaxOnly>{});
 #pragma unroll
       for (int b = 0; b < QB; ++b) m_ref[b] = m_seen[b];
+      run_pass(std::integral_constant<int, kPlain>{}, std::integral_constant<int, kPlain>{});
     }
 
     // Finalize: O^T register r of block d holds dim 32d + 8(r>>2) + 4half + (r&3).
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
       const int row = row0 + 32 * b + l32;
-      float l_tot;
-      if constexpr (kSumByMfma) {
-        // O^T register r of block DB-1 holds dim 32(DB-1) + 8(r>>2) + 4half + (r&3).
-        constexpr int rr = kOnesLane;  // offset of dim D inside the last block
-        constexpr int r = 4 * (rr >> 3) + (rr & 3);
-        const float v = o[b][C::DB - 1][r];
-        const float w = other_half(v);
-        l_tot = ((rr >> 2) & 1) == 0 ? (half == 0 ? v : w) : (half == 1 ? v : w);
-      } else {
-        l_tot = l_run[b] + other_half(l_run[b]);
-      }
+      const float l_tot = row_total(b);
       if (row < len) {
         const float inv = 1.f / l_tot;
         u16* op = out + size_t(start + row) * tok_stride + size_t(h) * D;

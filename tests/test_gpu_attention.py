@@ -219,3 +219,16 @@ def test_logit_jump_after_first_tile(D):
     got, _ = _gpu_attn(x, wl)
     want = oracle.varlen_attention(x.q, x.k, x.v, x.cu_seqlens, wl.softmax_scale)
     assert_attn_close(got, want, "bf16", f"logit jump D={D}")
+
+
+SHORT = [1, 2, 31, 32, 33, 0, 63, 64, 17, 48]
+
+
+@pytest.mark.parametrize("D", [32, 64, 80, 96, 128])
+def test_short_segments(D):
+    """Many segments shorter than one key tile or one query block."""
+    wl, x = _inputs(SHORT, H=4, D=D, dtype="bf16", seed=20 + D)
+    got, guard = _gpu_attn(x, wl, guard_rows=8, out_fill=9.0)
+    want = oracle.varlen_attention(x.q, x.k, x.v, x.cu_seqlens, wl.softmax_scale)
+    assert_attn_close(got, want, "bf16", f"short segments D={D}")
+    assert np.all(guard == 9.0)

@@ -262,6 +262,8 @@ def main():
     pre_avg_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in side]))
     wl_avg_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in side]))
 
+    ceiling = mfma_ceiling(lib, torch, dev, stream) if is_bf16_dtype(wl) else None
+
     # Correctness guard on the measured buffers: finite output, no work-list errors.
     meta = plan.meta.cpu().numpy()
     if int(meta[1]) != 0 or not torch.isfinite(out).all().item():
@@ -311,9 +313,48 @@ def main():
                     "frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "bytes_per_launch": pre_bytes},
         "step_frac_of_peak": round(value / peak, 4),
     }
+    if ceiling is not None:
+        result["mfma_ceiling"] = ceiling
+        result["roofline"]["frac_of_random_operand_ceiling"] = round(achieved / ceiling["random_bf16"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def is_bf16_dtype(wl):
+    return wl.dtype == "bf16"
+
+
+def mfma_ceiling(lib, torch, dev, stream):
+    """Sustained bf16 MFMA rate of a kernel that does nothing but MFMAs, on
+    operands drawn like the workload's inputs (N(0,1) rounded to bf16) and on
+    zeros.  The chip lowers its clock when operands toggle many bits, so the
+    first figure is what any bf16 MFMA kernel can reach on such data."""
+    from vision_encoder_varlen_amd import _lib
+    nbytes = 4 << 20
+    gen = torch.Generator(device="cpu").manual_seed(0)
+    rnd = torch.randn(nbytes // 2, generator=gen).to(torch.bfloat16).to(dev)
+    zero = torch.zeros(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    blocks, iters = 512, 1500
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    flops = blocks * 4 * 32 * iters * 32768.0
+    out = {}
+    for name, buf in (("random_bf16", rnd), ("zeros", zero)):
+        times = []
+        for _ in range(5):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            _lib.check(lib.vit_probe_mfma(buf.data_ptr(), nbytes, blocks, iters, sink.data_ptr(),
+                                          stream.cuda_stream))
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        best = min(times[2:])  # the clock settles over the first launches
+        out[name] = round(flops / (best * 1e-3) / 1e12, 1)
+    out["unit"] = "TFLOP/s"
+    out["probe"] = "vit_probe_mfma: 512 workgroups x 4 waves, 4 independent 32x32x16 bf16 chains per wave"
+    return out
 
 
 def _traffic_path(workload):

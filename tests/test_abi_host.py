@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
     for required in ("vit_qk_norm_rope", "vit_varlen_attn", "vit_varlen_attn_f32",
                      "vit_varlen_worklist", "vit_varlen_attn_planned", "vit_attn_block_m",
                      "vit_worklist_capacity", "vit_device_error", "vit_last_error", "vit_release",
-                     "vit_time_next_kernel"):
+                     "vit_time_next_kernel", "vit_probe_mfma"):
         assert required in names
     assert sorted(_lib.SIGNATURES) == names
 
@@ -141,3 +141,14 @@ def test_timing_hook_needs_both_events_or_neither(lib):
     assert "both" in _err(lib)
     assert lib.vit_time_next_kernel(None, FAKE) == _lib.VIT_ERR_INVALID_ARG
     assert lib.vit_time_next_kernel(None, None) == _lib.VIT_OK
+
+
+def test_probe_argument_errors(lib):
+    f = lib.vit_probe_mfma
+    big = 4 << 20
+    assert f(None, big, 8, 10, FAKE, None) == _lib.VIT_ERR_INVALID_ARG
+    assert f(FAKE, big - 16, 8, 10, FAKE, None) == _lib.VIT_ERR_INVALID_ARG
+    assert "bytes" in _err(lib)
+    assert f(FAKE, big, 0, 10, FAKE, None) == _lib.VIT_ERR_INVALID_ARG
+    assert f(FAKE, big, 8, 0, FAKE, None) == _lib.VIT_ERR_INVALID_ARG
+    assert f(FAKE + 8, big, 8, 10, FAKE, None) == _lib.VIT_ERR_INVALID_ARG

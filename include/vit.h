@@ -91,6 +91,21 @@ int vit_qk_norm_rope(void* q, void* k, int64_t total_tokens, int num_heads, int 
                      const float* k_weight, float eps, hipStream_t stream);
 
 /*
+ * vit_qk_norm_rope followed by vit_varlen_worklist, in one kernel launch: the
+ * two are independent, so one extra workgroup of the pre-pass launch builds
+ * the work-list while the others normalise and rotate q and k.  Arguments,
+ * results and errors are exactly those of the two calls (checked before
+ * anything is enqueued).  A list whose build needs more than 24 KiB of LDS
+ * (num_seqs > 2048) gets a launch of its own, as does a list when the
+ * pre-pass has nothing to do.
+ */
+int vit_qk_norm_rope_worklist(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
+                              int dtype, const int32_t* pos, float theta, const float* q_weight,
+                              const float* k_weight, float eps, const int32_t* cu_seqlens,
+                              int num_seqs, int max_seqlen, int block_m, int32_t* items,
+                              int64_t cap, int32_t* meta, hipStream_t stream);
+
+/*
  * Varlen attention, bf16 in and out, fp32 accumulation and softmax.
  *
  * For every segment i, head h and query a in the segment:
@@ -190,7 +205,8 @@ const char* vit_last_error(void);
 
 /*
  * Timing hook for profilers and benchmarks.  The next call on this host thread
- * of vit_qk_norm_rope, vit_varlen_worklist, vit_varlen_attn_planned,
+ * of vit_qk_norm_rope, vit_qk_norm_rope_worklist (its combined launch),
+ * vit_varlen_worklist, vit_varlen_attn_planned,
  * vit_varlen_attn or vit_varlen_attn_f32 records `start` when its kernel's
  * dispatch begins and `stop` when that kernel ends (hipExtLaunchKernel's
  * dispatch timestamps: the kernel alone, without launch gaps); the hook is

@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
     for required in ("vit_qk_norm_rope", "vit_varlen_attn", "vit_varlen_attn_f32",
                      "vit_varlen_worklist", "vit_varlen_attn_planned", "vit_attn_block_m",
                      "vit_worklist_capacity", "vit_device_error", "vit_last_error", "vit_release",
-                     "vit_time_next_kernel", "vit_probe_mfma"):
+                     "vit_time_next_kernel", "vit_probe_mfma", "vit_qk_norm_rope_worklist"):
         assert required in names
     assert sorted(_lib.SIGNATURES) == names
 
@@ -152,3 +152,17 @@ def test_probe_argument_errors(lib):
     assert f(FAKE, big, 0, 10, FAKE, None) == _lib.VIT_ERR_INVALID_ARG
     assert f(FAKE, big, 8, 0, FAKE, None) == _lib.VIT_ERR_INVALID_ARG
     assert f(FAKE + 8, big, 8, 10, FAKE, None) == _lib.VIT_ERR_INVALID_ARG
+
+
+def test_fused_prepass_worklist_checks_both_argument_sets(lib):
+    f = lib.vit_qk_norm_rope_worklist
+    meta = FAKE + 0x40
+    ok_pre = (FAKE, FAKE + 0x1000, 16, 2, 64, 1, None, 1e4, None, None, 1e-6)
+    ok_wl = (FAKE, 3, 10, 64, FAKE, 3, meta, None)
+    assert f(None, *ok_pre[1:], *ok_wl) == _lib.VIT_ERR_INVALID_ARG          # pre-pass check
+    assert "q or k" in _err(lib)
+    bad_dim = ok_pre[:4] + (60,) + ok_pre[5:]
+    assert f(*bad_dim, *ok_wl) == _lib.VIT_ERR_UNSUPPORTED
+    assert f(*ok_pre, FAKE, 3, 200, 64, FAKE, 3, meta, None) == _lib.VIT_ERR_INVALID_ARG  # capacity
+    assert "capacity" in _err(lib)
+    assert f(*ok_pre, FAKE, 9000, 10, 64, FAKE, 9000, meta, None) == _lib.VIT_ERR_UNSUPPORTED

@@ -220,6 +220,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
 
   const int64_t nunits = int64_t(meta[0]) * H;
   for (int64_t unit = blockIdx.x; unit < nunits; unit += gridDim.x) {
+    // The previous unit's output stores (and any copies) are complete, so
+    // from here on this wave's vector-memory counter holds only this unit's
+    // Q loads, then its tile copies, in issue order.
+    __builtin_amdgcn_s_waitcnt(0);
     const int item = int(unit / H);
     const int h = int(unit - int64_t(item) * H);
     const int seg = items[2 * item];
@@ -427,10 +431,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
         for (int d = 0; d < C::DB; ++d) o[b][d] = f32x16_t{};
         l_run[b] = 0.f;  // this lane's partial row sum
       }
-      // Nothing of ours may be in flight when the copy pipeline starts
-      // counting, and the previous unit's (or pass's) last tile must no
-      // longer be read.
-      __builtin_amdgcn_s_waitcnt(0);
+      // The previous unit's (or pass's) last tile must no longer be read.
+      // The Q loads may still be in flight: loads complete in issue order, so
+      // a copy wait (vmcnt) also covers the older Q loads, and the first
+      // tile's copies overlap them.
       __syncthreads();
 #pragma unroll
       for (int t = 0; t < STAGES - 1; ++t)

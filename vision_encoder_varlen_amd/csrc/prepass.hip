@@ -29,6 +29,7 @@
 #include <stdint.h>
 
 #include "vit_kernels.h"
+#include "worklist_build.h"
 
 namespace vit {
 namespace {
@@ -104,8 +105,20 @@ template <typename T, int E>
 __global__ __launch_bounds__(kThreads) void prepass_kernel(
     T* __restrict__ q, T* __restrict__ k, long long T_tok, int H, int D, int G, int tok_per_grp,
     const int32_t* __restrict__ pos, Freqs freqs, const float* __restrict__ wq,
-    const float* __restrict__ wk, float eps) {
+    const float* __restrict__ wk, float eps, WorklistJob job) {
   extern __shared__ float2 cs[];  // [tok_per_grp][D/2] (cos, sin)
+  __shared__ int s_wave[kThreads / 64];
+  // With a work-list job workgroup 0 (dispatched first) builds the list,
+  // independent of the pre-pass, and the others share the token groups.
+  const int npre = job.cu != nullptr ? int(gridDim.x) - 1 : int(gridDim.x);
+  const int pblock = job.cu != nullptr ? int(blockIdx.x) - 1 : int(blockIdx.x);
+  if (pblock < 0) {
+    unsigned long long* keys = reinterpret_cast<unsigned long long*>(cs);
+    wl::build_worklist<kThreads>(job.cu, job.N, job.npad, job.max_seqlen, job.block_m, job.items,
+                                 job.cap, job.meta, keys, reinterpret_cast<int*>(keys + job.npad),
+                                 s_wave);
+    return;
+  }
   const int tid = threadIdx.x;
   const int half_d = D / 2;
   const int quarter_d = D / 4;
@@ -134,8 +147,8 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
     }
   }
 
-  for (long long t0 = (long long)blockIdx.x * tok_per_grp; t0 < T_tok;
-       t0 += (long long)gridDim.x * tok_per_grp) {
+  for (long long t0 = (long long)pblock * tok_per_grp; t0 < T_tok;
+       t0 += (long long)npre * tok_per_grp) {
     const int ntok = T_tok - t0 < tok_per_grp ? int(T_tok - t0) : tok_per_grp;
     if (rope) {
       for (int i = tid; i < ntok * half_d; i += kThreads) {
@@ -222,8 +235,15 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
 hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
                           const int32_t* pos, const double* inv_freq_host, const float* wq,
                           const float* wk, float eps, hipStream_t stream, hipEvent_t e0,
-                          hipEvent_t e1) {
-  if (T <= 0 || (pos == nullptr && wq == nullptr)) return hipSuccess;
+                          hipEvent_t e1, const WorklistJob* job) {
+  WorklistJob jb{};
+  if (job != nullptr) jb = *job;
+  const bool prepass_work = T > 0 && (pos != nullptr || wq != nullptr);
+  if (!prepass_work) {
+    if (jb.cu == nullptr) return hipSuccess;
+    return launch_worklist(jb.cu, jb.N, jb.max_seqlen, jb.block_m, jb.items, jb.cap, jb.meta,
+                           stream, e0, e1);
+  }
   // Elements per lane per half row: 8 (one 16-byte access) for bf16 rows
   // whose half is a multiple of 8, else 4.  G lanes cover a row.
   const int E = (dtype == 1 && (D / 2) % 8 == 0) ? 8 : 4;
@@ -243,20 +263,36 @@ hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
     }
   }
   const long long groups = (T + tok_per_grp - 1) / tok_per_grp;
-  const long long grid = groups < 65536 ? groups : 65536;
-  const size_t lds = pos != nullptr ? size_t(tok_per_grp) * (D / 2) * sizeof(float) * 2 : 0;
+  long long grid = groups < 65536 ? groups : 65536;
+  size_t lds = pos != nullptr ? size_t(tok_per_grp) * (D / 2) * sizeof(float) * 2 : 0;
+  if (jb.cu != nullptr) {
+    // One more workgroup builds the work-list in the same launch.
+    jb.npad = 1;
+    while (jb.npad < jb.N) jb.npad <<= 1;
+    const size_t wl_lds = size_t(jb.npad) * (sizeof(unsigned long long) + sizeof(int));
+    if (wl_lds > kFusedWorklistMaxLds) {
+      // Too large to share the pre-pass's LDS budget: two launches.
+      const hipError_t e = launch_worklist(jb.cu, jb.N, jb.max_seqlen, jb.block_m, jb.items, jb.cap,
+                                           jb.meta, stream, nullptr, nullptr);
+      if (e != hipSuccess) return e;
+      jb = WorklistJob{};
+    } else {
+      grid += 1;
+      if (wl_lds > lds) lds = wl_lds;
+    }
+  }
   if (dtype == 1 && E == 8) {
     hipExtLaunchKernelGGL(prepass_kernel<u16, 8>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
                           e0, e1, 0, static_cast<u16*>(q), static_cast<u16*>(k), (long long)T, H, D,
-                          G, tok_per_grp, pos, fr, wq, wk, eps);
+                          G, tok_per_grp, pos, fr, wq, wk, eps, jb);
   } else if (dtype == 1) {
     hipExtLaunchKernelGGL(prepass_kernel<u16, 4>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
                           e0, e1, 0, static_cast<u16*>(q), static_cast<u16*>(k), (long long)T, H, D,
-                          G, tok_per_grp, pos, fr, wq, wk, eps);
+                          G, tok_per_grp, pos, fr, wq, wk, eps, jb);
   } else {
     hipExtLaunchKernelGGL(prepass_kernel<float, 4>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
                           e0, e1, 0, static_cast<float*>(q), static_cast<float*>(k), (long long)T, H,
-                          D, G, tok_per_grp, pos, fr, wq, wk, eps);
+                          D, G, tok_per_grp, pos, fr, wq, wk, eps, jb);
   }
   return hipGetLastError();
 }

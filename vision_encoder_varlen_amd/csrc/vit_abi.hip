@@ -158,14 +158,9 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, 
   return ok();
 }
 
-}  // namespace
-
-extern "C" {
-
-int vit_qk_norm_rope(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
-                     int dtype, const int32_t* pos, float theta, const float* q_weight,
-                     const float* k_weight, float eps, hipStream_t stream) {
-  const TimingHook t = take_timing();
+int check_prepass_args(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
+                       int dtype, const int32_t* pos, float theta, const float* q_weight,
+                       const float* k_weight, float eps) {
   if (!q || !k) return fail(VIT_ERR_INVALID_ARG, "null q or k");
   if (total_tokens < 0) return fail(VIT_ERR_INVALID_ARG, "total_tokens must be >= 0");
   if (num_heads < 1) return fail(VIT_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", num_heads);
@@ -183,7 +178,35 @@ int vit_qk_norm_rope(void* q, void* k, int64_t total_tokens, int num_heads, int 
     return fail(VIT_ERR_INVALID_ARG, "norm weights must be 16-byte aligned");
   if (pos && !aligned4(pos)) return fail(VIT_ERR_INVALID_ARG, "pos must be 4-byte aligned");
   if (q == k) return fail(VIT_ERR_INVALID_ARG, "q and k must be distinct buffers");
-  if (total_tokens == 0 || (pos == nullptr && q_weight == nullptr)) {
+  return VIT_OK;
+}
+
+int check_worklist_args(const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int block_m,
+                        int32_t* items, int64_t cap, int32_t* meta) {
+  if (!cu_seqlens || !items || !meta) return fail(VIT_ERR_INVALID_ARG, "null pointer argument");
+  if (num_seqs < 0 || max_seqlen < 0) return fail(VIT_ERR_INVALID_ARG, "negative size");
+  if (num_seqs > vit::kWorklistMaxSeqs)
+    return fail(VIT_ERR_UNSUPPORTED, "num_seqs %d exceeds the supported maximum %d", num_seqs,
+                vit::kWorklistMaxSeqs);
+  if (block_m <= 0) return fail(VIT_ERR_INVALID_ARG, "block_m must be > 0");
+  const int64_t need = capacity(num_seqs, max_seqlen, block_m);
+  if (need > kMaxCapacity) return fail(VIT_ERR_UNSUPPORTED, "work-list capacity %lld too large", (long long)need);
+  if (cap < need)
+    return fail(VIT_ERR_INVALID_ARG, "cap %lld below the required capacity %lld", (long long)cap,
+                (long long)need);
+  if (!aligned4(cu_seqlens) || !aligned4(items) || !aligned4(meta))
+    return fail(VIT_ERR_INVALID_ARG, "int32 buffers must be 4-byte aligned");
+  return VIT_OK;
+}
+
+// Arguments already checked.  job: a work-list to build in the same launch,
+// or null.
+int launch_prepass_job(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
+                       int dtype, const int32_t* pos, float theta, const float* q_weight,
+                       const float* k_weight, float eps, const vit::WorklistJob* job,
+                       hipStream_t stream, const TimingHook& t) {
+  const bool prepass_work = total_tokens > 0 && (pos != nullptr || q_weight != nullptr);
+  if (!prepass_work && job == nullptr) {
     const hipError_t e = record_empty(t, stream);
     return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
   }
@@ -191,10 +214,41 @@ int vit_qk_norm_rope(void* q, void* k, int64_t total_tokens, int num_heads, int 
   double inv_freq[64];
   const int F = head_dim / 4;
   for (int j = 0; j < F; ++j) inv_freq[j] = std::pow(double(theta), -2.0 * j / (head_dim / 2.0));
-  hipError_t e = vit::launch_prepass(q, k, total_tokens, num_heads, head_dim, dtype, pos,
-                                     inv_freq, q_weight, k_weight, eps, stream, t.start, t.stop);
-  if (e != hipSuccess) return hip_fail(e, "pre-pass launch");
+  hipError_t e = vit::launch_prepass(q, k, total_tokens, num_heads, head_dim, dtype, pos, inv_freq,
+                                     q_weight, k_weight, eps, stream, t.start, t.stop, job);
+  if (e != hipSuccess) return hip_fail(e, job ? "pre-pass + work-list launch" : "pre-pass launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int vit_qk_norm_rope(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
+                     int dtype, const int32_t* pos, float theta, const float* q_weight,
+                     const float* k_weight, float eps, hipStream_t stream) {
+  const TimingHook t = take_timing();
+  const int rc = check_prepass_args(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta,
+                                    q_weight, k_weight, eps);
+  if (rc != VIT_OK) return rc;
+  return launch_prepass_job(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta, q_weight,
+                            k_weight, eps, nullptr, stream, t);
+}
+
+int vit_qk_norm_rope_worklist(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
+                              int dtype, const int32_t* pos, float theta, const float* q_weight,
+                              const float* k_weight, float eps, const int32_t* cu_seqlens,
+                              int num_seqs, int max_seqlen, int block_m, int32_t* items,
+                              int64_t cap, int32_t* meta, hipStream_t stream) {
+  const TimingHook t = take_timing();
+  int rc = check_prepass_args(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta, q_weight,
+                              k_weight, eps);
+  if (rc != VIT_OK) return rc;
+  rc = check_worklist_args(cu_seqlens, num_seqs, max_seqlen, block_m, items, cap, meta);
+  if (rc != VIT_OK) return rc;
+  const vit::WorklistJob job{cu_seqlens, num_seqs, 0, max_seqlen, block_m, items, cap, meta};
+  return launch_prepass_job(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta, q_weight,
+                            k_weight, eps, &job, stream, t);
 }
 
 int vit_varlen_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
@@ -227,19 +281,8 @@ int64_t vit_worklist_capacity(int num_seqs, int max_seqlen, int block_m) {
 int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int block_m,
                         int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream) {
   const TimingHook t = take_timing();
-  if (!cu_seqlens || !items || !meta) return fail(VIT_ERR_INVALID_ARG, "null pointer argument");
-  if (num_seqs < 0 || max_seqlen < 0) return fail(VIT_ERR_INVALID_ARG, "negative size");
-  if (num_seqs > vit::kWorklistMaxSeqs)
-    return fail(VIT_ERR_UNSUPPORTED, "num_seqs %d exceeds the supported maximum %d", num_seqs,
-                vit::kWorklistMaxSeqs);
-  if (block_m <= 0) return fail(VIT_ERR_INVALID_ARG, "block_m must be > 0");
-  const int64_t need = capacity(num_seqs, max_seqlen, block_m);
-  if (need > kMaxCapacity) return fail(VIT_ERR_UNSUPPORTED, "work-list capacity %lld too large", (long long)need);
-  if (cap < need)
-    return fail(VIT_ERR_INVALID_ARG, "cap %lld below the required capacity %lld", (long long)cap,
-                (long long)need);
-  if (!aligned4(cu_seqlens) || !aligned4(items) || !aligned4(meta))
-    return fail(VIT_ERR_INVALID_ARG, "int32 buffers must be 4-byte aligned");
+  const int rc = check_worklist_args(cu_seqlens, num_seqs, max_seqlen, block_m, items, cap, meta);
+  if (rc != VIT_OK) return rc;
   hipError_t e = vit::launch_worklist(cu_seqlens, num_seqs, max_seqlen, block_m, items, cap, meta,
                                       stream, t.start, t.stop);
   if (e != hipSuccess) return hip_fail(e, "work-list launch");

@@ -31,12 +31,31 @@ inline bool attn_head_dim_supported(int D) {
   return D == 32 || D == 64 || D == 80 || D == 96 || D == 128;
 }
 
+// A work-list build to run in the same launch as the pre-pass (cu == null:
+// none).  npad is filled in by launch_prepass.
+struct WorklistJob {
+  const int32_t* cu;
+  int N;
+  int npad;
+  int max_seqlen;
+  int block_m;
+  int32_t* items;
+  long long cap;
+  int32_t* meta;
+};
+// Largest work-list LDS (npad * 12 bytes) built inside the pre-pass launch;
+// larger lists get a launch of their own.
+constexpr size_t kFusedWorklistMaxLds = 24 * 1024;
+
 // Pre-pass: inv_freq_host holds the D/4 rotary inverse frequencies in double
-// (may be null when pos is null).  dtype: 0 = fp32, 1 = bf16.
+// (may be null when pos is null).  dtype: 0 = fp32, 1 = bf16.  With a job,
+// the work-list is built by one more workgroup of the same launch (the two
+// are independent).
 hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
                           const int32_t* pos, const double* inv_freq_host,
                           const float* wq, const float* wk, float eps, hipStream_t stream,
-                          hipEvent_t ev_start, hipEvent_t ev_stop);
+                          hipEvent_t ev_start, hipEvent_t ev_stop,
+                          const WorklistJob* job = nullptr);
 
 hipError_t launch_worklist(const int32_t* cu, int N, int max_seqlen, int block_m,
                            int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream,

@@ -24,37 +24,10 @@
 #include <stdint.h>
 
 #include "vit_kernels.h"
+#include "worklist_build.h"
 
 namespace vit {
 namespace {
-
-constexpr unsigned long long kEmpty = ~0ull;
-
-// Exclusive prefix over the workgroup of one int per thread, plus the total:
-// a shuffle scan inside each wave, then the wave totals through LDS (one
-// barrier).
-template <int THREADS>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
-  }
-  if (lane == 63) s_wave[wave] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < THREADS / 64; ++w) {
-    const int t = s_wave[w];
-    before += w < wave ? t : 0;
-    all += t;
-  }
-  *total = all;
-  return before + incl - v;
-}
 
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void worklist_kernel(
@@ -63,96 +36,7 @@ __global__ __launch_bounds__(THREADS) void worklist_kernel(
   extern __shared__ __align__(16) unsigned long long keys[];  // [npad]
   int* const offs = reinterpret_cast<int*>(keys + npad);       // [npad] exclusive tile offsets
   __shared__ int s_wave[THREADS / 64];
-
-  const int tid = threadIdx.x;
-  // Every thread reads cu[0] with its own entries: one round trip to memory.
-  const bool cu0_bad = N > 0 && cu[0] != 0;
-  int err = cu0_bad ? 1 : 0;
-
-  // 1. keys: high word = 0x7fffffff - len (ascending = longest first), low = index.
-  for (int i = tid; i < npad; i += THREADS) {
-    unsigned long long key = kEmpty;
-    if (i < N && !cu0_bad) {
-      const int len = cu[i + 1] - cu[i];
-      if (len < 0) {
-        err |= 2;
-      } else if (len > max_seqlen) {
-        err |= 4;
-      } else if (len > 0) {
-        key = (static_cast<unsigned long long>(0x7fffffffu - static_cast<unsigned>(len)) << 32) |
-              static_cast<unsigned>(i);
-      }
-    }
-    keys[i] = key;
-  }
-  const int err_any = __syncthreads_or(err & 2) ? 2 : 0;
-  const int err_long = __syncthreads_or(err & 4) ? 4 : 0;
-
-  // 2. sort only when needed.
-  int unsorted = 0;
-  for (int i = tid; i + 1 < npad; i += THREADS)
-    if (keys[i] > keys[i + 1]) unsorted = 1;
-  if (__syncthreads_or(unsorted)) {
-    for (int size = 2; size <= npad; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < npad; i += THREADS) {
-          const int j = i ^ stride;
-          if (j > i) {
-            const unsigned long long a = keys[i], b = keys[j];
-            const bool ascending = (i & size) == 0;
-            if ((a > b) == ascending) {
-              keys[i] = b;
-              keys[j] = a;
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
-  }
-
-  // 3. exclusive scan of tile counts: each thread owns a contiguous chunk.
-  const int chunk = (npad + THREADS - 1) / THREADS;
-  const int c0 = tid * chunk;
-  int local = 0;
-  for (int i = c0; i < c0 + chunk && i < npad; ++i) {
-    const unsigned long long key = keys[i];
-    int nt = 0;
-    if (key != kEmpty) {
-      const int len = int(0x7fffffffu - static_cast<unsigned>(key >> 32));
-      nt = (len + block_m - 1) / block_m;
-    }
-    offs[i] = nt;
-    local += nt;
-  }
-  int total = 0;
-  int run = block_exclusive_scan<THREADS>(local, s_wave, &total);
-  for (int i = c0; i < c0 + chunk && i < npad; ++i) {
-    const int nt = offs[i];
-    offs[i] = run;
-    run += nt;
-  }
-
-  // 4. scatter (each thread reads back only the offsets it wrote).
-  const bool overflow = static_cast<long long>(total) > cap;
-  if (!overflow) {
-    for (int i = c0; i < c0 + chunk && i < npad; ++i) {
-      const unsigned long long key = keys[i];
-      if (key == kEmpty) continue;
-      const int seg = int(key & 0xffffffffu);
-      const int len = int(0x7fffffffu - static_cast<unsigned>(key >> 32));
-      const int nt = (len + block_m - 1) / block_m;
-      const int base = offs[i];
-      for (int j = 0; j < nt; ++j) {
-        items[2 * (base + j)] = seg;
-        items[2 * (base + j) + 1] = j;
-      }
-    }
-  }
-  if (tid == 0) {
-    meta[0] = overflow ? 0 : total;
-    meta[1] = (cu0_bad ? 1 : 0) | err_any | err_long | (overflow ? 8 : 0);
-  }
+  wl::build_worklist<THREADS>(cu, N, npad, max_seqlen, block_m, items, cap, meta, keys, offs, s_wave);
 }
 
 template <int THREADS>

@@ -39,10 +39,7 @@ def dtype_code(dtype: torch.dtype) -> int:
     return _DTYPES[dtype]
 
 
-def qk_norm_rope_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch.Tensor] = None,
-                  theta: float = 10000.0, q_weight: Optional[torch.Tensor] = None,
-                  k_weight: Optional[torch.Tensor] = None, eps: float = 1e-6) -> None:
-    """In-place Q/K RMSNorm (when weights are given) then 2D rotary (when ``pos`` is given)."""
+def _prepass_checks(q, k, pos, q_weight, k_weight) -> None:
     _need_cuda("q", q)
     _need_cuda("k", k, q.dtype)
     if q.dim() != 3 or k.shape != q.shape:
@@ -57,9 +54,35 @@ def qk_norm_rope_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch.Tensor] 
             _need_cuda(name, w, torch.float32)
             if w.shape != (D,):
                 raise ValueError(f"{name} must be float32 [D]")
+
+
+def qk_norm_rope_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch.Tensor] = None,
+                  theta: float = 10000.0, q_weight: Optional[torch.Tensor] = None,
+                  k_weight: Optional[torch.Tensor] = None, eps: float = 1e-6) -> None:
+    """In-place Q/K RMSNorm (when weights are given) then 2D rotary (when ``pos`` is given)."""
+    _prepass_checks(q, k, pos, q_weight, k_weight)
+    T, H, D = q.shape
     _lib.check(_lib.load().vit_qk_norm_rope(
         q.data_ptr(), k.data_ptr(), T, H, D, dtype_code(q.dtype), _ptr(pos), float(theta),
         _ptr(q_weight), _ptr(k_weight), float(eps), _stream(q)))
+
+
+def qk_norm_rope_worklist_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch.Tensor],
+                           theta: float, q_weight: Optional[torch.Tensor],
+                           k_weight: Optional[torch.Tensor], eps: float, plan: "Plan",
+                           cu_seqlens: torch.Tensor) -> "Plan":
+    """``qk_norm_rope_`` and ``rebuild_worklist(plan, cu_seqlens)`` in one launch."""
+    _prepass_checks(q, k, pos, q_weight, k_weight)
+    _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
+    if cu_seqlens.numel() - 1 != plan.num_seqs:
+        raise ValueError("cu_seqlens does not match the plan")
+    T, H, D = q.shape
+    _lib.check(_lib.load().vit_qk_norm_rope_worklist(
+        q.data_ptr(), k.data_ptr(), T, H, D, dtype_code(q.dtype), _ptr(pos), float(theta),
+        _ptr(q_weight), _ptr(k_weight), float(eps), cu_seqlens.data_ptr(), plan.num_seqs,
+        plan.max_seqlen, plan.block_m, plan.items.data_ptr(), plan.cap, plan.meta.data_ptr(),
+        _stream(q)))
+    return plan
 
 
 def _attn_checks(q, k, v, cu_seqlens):

@@ -197,7 +197,11 @@ def main():
                plan.meta.data_ptr(), sh)
     at_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), cu.data_ptr(), plan.items.data_ptr(),
                plan.cap, plan.meta.data_ptr(), H, D, float(wl.softmax_scale), dcode,
-               out.data_ptr(), sh)
+               out.data_ptr(), None, sh)
+    # The same attention call that also writes the log-sum-exp rows (timed
+    # outside the timed loop, for its overhead).
+    lse_buf = torch.empty((T, H), dtype=torch.float32, device=dev)
+    at_lse_args = at_args[:-2] + (lse_buf.data_ptr(), sh)
     # The step's first launch: pre-pass and work-list build together.
     fused_args = pre_args[:-1] + wl_args
     f_pre, f_wl, f_at = lib.vit_qk_norm_rope, lib.vit_varlen_worklist, lib.vit_varlen_attn_planned
@@ -253,7 +257,7 @@ def main():
     # Outside the timed region: the pre-pass and work-list kernels' own
     # durations, from the same dispatch-timestamp events (each hooked launch
     # adds a launch gap, so they are not hooked inside the timed loop).
-    side = [new_events(6) for _ in range(K)]
+    side = [new_events(8) for _ in range(K)]
     torch.cuda.synchronize()
     for e in side:
         check(f_hook(e[0].cuda_event, e[1].cuda_event))
@@ -262,11 +266,13 @@ def main():
         check(f_wl(*wl_args))
         check(f_hook(e[4].cuda_event, e[5].cuda_event))
         check(f_fused(*fused_args))
-        check(f_at(*at_args))
+        check(f_hook(e[6].cuda_event, e[7].cuda_event))
+        check(f_at(*at_lse_args))
     torch.cuda.synchronize()
     pre_avg_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in side]))
     wl_avg_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in side]))
     fused_avg_ms = float(np.mean([e[4].elapsed_time(e[5]) for e in side]))
+    lse_avg_ms = float(np.mean([e[6].elapsed_time(e[7]) for e in side]))
 
     ceiling = mfma_ceiling(lib, torch, dev, stream) if is_bf16_dtype(wl) else None
 
@@ -316,7 +322,8 @@ def main():
         "kernels_us": {"prepass_and_worklist_launch": round(fused_avg_ms * 1e3, 3),
                        "prepass_alone": round(pre_avg_ms * 1e3, 3),
                        "worklist_alone": round(wl_avg_ms * 1e3, 3),
-                       "attention": round(attn_avg_ms * 1e3, 3)},
+                       "attention": round(attn_avg_ms * 1e3, 3),
+                       "attention_with_lse": round(lse_avg_ms * 1e3, 3)},
         "prepass": {"bound": "hbm", "achieved": round(pre_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "bytes_per_launch": pre_bytes},
         "step_frac_of_peak": round(value / peak, 4),

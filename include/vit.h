@@ -139,6 +139,22 @@ int vit_varlen_attn_f32(const void* q, const void* k, const void* v, const int32
                         void* out, hipStream_t stream);
 
 /*
+ * vit_varlen_attn (dtype VIT_BF16) or vit_varlen_attn_f32 (VIT_F32) that also
+ * writes each row's log-sum-exp of scores, natural log:
+ *   lse[a, h] = log sum_b exp(scale * <q[a,h,:], k[b,h,:]>), b over a's segment
+ * -- the second result the tokenspeed page's FA4 varlen call returns next to
+ * the output (vision_attn_fa4) and that its cuDNN prefill call is asked for
+ * (return_lse in vision_attn_flashinfer_cudnn).  It lets partial results over
+ * key ranges be merged.
+ *  lse   fp32 [T, H] on the device, token-major like out, 4-byte aligned, not
+ *        aliasing q, k, v or out; rows outside the accepted segments are left
+ *        untouched.  Null: only out is written.
+ */
+int vit_varlen_attn_lse(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                        int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
+                        int dtype, void* out, float* lse, hipStream_t stream);
+
+/*
  * Query rows per (segment, q-tile) work item of the attention kernel for this
  * shape and dtype, or a negative VIT_ERR_* code for an unsupported shape.
  */
@@ -167,14 +183,14 @@ int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
  * Attention over a work-list built by vit_varlen_worklist with
  * block_m = vit_attn_block_m(num_heads, head_dim, dtype) for the same
  * cu_seqlens.  Lets one list serve every layer of an encoder tower.
- * dtype selects the bf16 (VIT_BF16) or fp32 (VIT_F32) kernel; the other
- * arguments are those of vit_varlen_attn, and cap is the capacity the list was
- * built with.
+ * dtype selects the bf16 (VIT_BF16) or fp32 (VIT_F32) kernel; lse is as for
+ * vit_varlen_attn_lse (null: not written); cap is the capacity the list was
+ * built with; the other arguments are those of vit_varlen_attn.
  */
 int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
                             const int32_t* cu_seqlens, const int32_t* items, int64_t cap,
                             const int32_t* meta, int num_heads, int head_dim, float scale,
-                            int dtype, void* out, hipStream_t stream);
+                            int dtype, void* out, float* lse, hipStream_t stream);
 
 /*
  * Reads (and with reset != 0 clears) the work-list error bits (enum

@@ -21,20 +21,23 @@ What it computes, and what the pages say about it:
   kernel is scheduled by.  The pages have no scheduler; this rule is the
   library's own and is stated in ``worklist.py``.
 * ``rounding`` -- storage rounding of fp64 results to bf16 / fp32.
+* ``segment_lse`` / ``varlen_lse`` -- the log-sum-exp of each row's scores
+  (natural log), the optional second result of the attention.
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 something other than itself (an independent formulation from the pages, a
 library routine, a closed form, brute force on tiny inputs, or an invariant).
 No function is "parity unpinned".
 """
-from .attention import segment_attention, varlen_attention, varlen_attention_rows
+from .attention import (segment_attention, segment_lse, varlen_attention,
+                        varlen_attention_rows, varlen_lse)
 from .prepass import (apply_rope_2d, qk_norm_rope, rms_norm, rope_angles,
                       rope_inv_freq)
 from .rounding import round_to_bf16, round_to_f32, round_to_dtype
 from .worklist import worklist
 
 __all__ = [
-    "segment_attention", "varlen_attention", "varlen_attention_rows",
+    "segment_attention", "segment_lse", "varlen_attention", "varlen_attention_rows", "varlen_lse",
     "apply_rope_2d", "qk_norm_rope", "rms_norm", "rope_angles", "rope_inv_freq",
     "round_to_bf16", "round_to_f32", "round_to_dtype", "worklist",
 ]

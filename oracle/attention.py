@@ -47,6 +47,39 @@ def segment_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float)
     return out
 
 
+def segment_lse(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """Log-sum-exp of one segment's scores: ``[s, H]`` (fp64, natural log).
+
+    ``lse[a, h] = log sum_b exp(scale * <q[a,h], k[b,h]>)`` over the segment's
+    keys -- the second result the tokenspeed page's FA4 varlen call can return
+    next to the output (``vision_attn_fa4``), and what ``return_lse`` asks the
+    cuDNN prefill call for (``vision_attn_flashinfer_cudnn``).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    s, H, _ = q.shape
+    out = np.empty((s, H), dtype=np.float64)
+    for h in range(H):
+        kh = k[:, h, :]
+        for r0 in range(0, s, _ROW_BLOCK):
+            scores = (q[r0:r0 + _ROW_BLOCK, h, :] @ kh.T) * scale
+            m = np.max(scores, axis=-1)
+            out[r0:r0 + _ROW_BLOCK, h] = m + np.log(np.sum(np.exp(scores - m[:, None]), axis=-1))
+    return out
+
+
+def varlen_lse(q: np.ndarray, k: np.ndarray, cu_seqlens: np.ndarray, scale: float) -> np.ndarray:
+    """Log-sum-exp ``[T, H]`` of every segment's scores; rows outside ``[0, cu[N])`` are NaN."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    q = np.asarray(q, dtype=np.float64)
+    out = np.full(q.shape[:2], np.nan, dtype=np.float64)
+    for i in range(len(cu) - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b > a:
+            out[a:b] = segment_lse(q[a:b], k[a:b], scale)
+    return out
+
+
 def varlen_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                      cu_seqlens: np.ndarray, scale: float) -> np.ndarray:
     """All segments of a packed batch; rows outside ``[0, cu[N])`` are NaN."""

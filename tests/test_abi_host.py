@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
     for required in ("vit_qk_norm_rope", "vit_varlen_attn", "vit_varlen_attn_f32",
                      "vit_varlen_worklist", "vit_varlen_attn_planned", "vit_attn_block_m",
                      "vit_worklist_capacity", "vit_device_error", "vit_last_error", "vit_release",
-                     "vit_time_next_kernel", "vit_probe_mfma", "vit_qk_norm_rope_worklist"):
+                     "vit_time_next_kernel", "vit_probe_mfma", "vit_qk_norm_rope_worklist",
+                     "vit_varlen_attn_lse"):
         assert required in names
     assert sorted(_lib.SIGNATURES) == names
 
@@ -113,11 +114,15 @@ def test_worklist_argument_errors(lib):
 
 def test_planned_argument_errors(lib):
     f = lib.vit_varlen_attn_planned
-    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None) == 1
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 5, FAKE + 0x100, None) == 1
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 5, FAKE + 0x100, None, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None, None) == 1
+    # lse must be aligned and must not alias the tensors
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, FAKE + 2, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, FAKE + 0x100, None) == 1
+    assert "alias" in _err(lib)
     # an empty plan is a no-op
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None) == 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None, None) == 0
 
 
 def test_empty_batch_is_a_no_op(lib):

@@ -232,3 +232,64 @@ def test_short_segments(D):
     want = oracle.varlen_attention(x.q, x.k, x.v, x.cu_seqlens, wl.softmax_scale)
     assert_attn_close(got, want, "bf16", f"short segments D={D}")
     assert np.all(guard == 9.0)
+
+
+# Log-sum-exp rows.  fp32: the kernel sums fp32 weights, so 1e-5 absolute (at
+# |lse| up to ~10) covers its rounding.  bf16: inputs are exact bf16 values and
+# the scores are fp32 MFMA sums; the row sum is of fp32 weights except for head
+# dims that are not a multiple of 32, where it comes from the P V MFMA with
+# bf16-rounded weights (relative error up to 2^-9 per weight), so the bound is
+# 2^-8 absolute on lse.
+LSE_TOL = {"f32": 1e-5, "bf16": 2.0 ** -8}
+
+
+@pytest.mark.parametrize("D", [32, 64, 80, 96, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_lse_matches_oracle(D, dtype):
+    import torch
+    from vision_encoder_varlen_amd import ops
+    wl, x = _inputs(RAGGED + [0, 2], H=3, D=D, dtype=dtype, seed=40 + D)
+    q, k, v = (to_dev(a, dtype) for a in (x.q, x.k, x.v))
+    cu = torch.from_numpy(x.cu_seqlens).cuda()
+    lse = torch.full((wl.total_tokens, 3), float("nan"), dtype=torch.float32, device="cuda")
+    out = ops.varlen_attn(q, k, v, cu, wl.max_seqlen, wl.softmax_scale, lse=lse)
+    torch.cuda.synchronize()
+    want = oracle.varlen_lse(x.q, x.k, x.cu_seqlens, wl.softmax_scale)
+    got = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - want)) <= LSE_TOL[dtype]
+    # the output is the same as without lse
+    plain, _ = _gpu_attn(x, wl)
+    assert np.array_equal(to_host(out), plain)
+
+
+def test_lse_planned_and_after_a_repeat_pass():
+    """Planned call, and a batch whose later keys force the exact-max repeat."""
+    import torch
+    from vision_encoder_varlen_amd import ops
+    D = 128
+    lens = [300, 97]
+    wl = W.from_seqlens(lens, H=2, D=D, dtype="bf16", seed=13)
+    x = W.generate(wl)
+    u = np.zeros(D, dtype=np.float32)
+    u[: D // 2] = 1.0
+    u /= np.linalg.norm(u)
+    big = 4.0 * np.sqrt(D)
+    x.q = np.broadcast_to(big * u, (sum(lens), 2, D)).astype(np.float32).copy()
+    k = x.k * 0.01
+    k[:64] -= big * u
+    k[300:364] -= big * u
+    k[200:210] += big * u
+    from vision_encoder_varlen_amd.workloads import bf16_bits_to_f32, f32_to_bf16_bits
+    x.q = bf16_bits_to_f32(f32_to_bf16_bits(x.q)).reshape(x.q.shape)
+    x.k = bf16_bits_to_f32(f32_to_bf16_bits(k)).reshape(k.shape)
+    q, kk, v = (to_dev(a, "bf16") for a in (x.q, x.k, x.v))
+    cu = torch.from_numpy(x.cu_seqlens).cuda()
+    plan = ops.varlen_worklist(cu, wl.max_seqlen, ops.attn_block_m(2, D, q.dtype))
+    lse = torch.empty((sum(lens), 2), dtype=torch.float32, device="cuda")
+    ops.varlen_attn_planned(q, kk, v, cu, plan, wl.softmax_scale, lse=lse)
+    torch.cuda.synchronize()
+    want = oracle.varlen_lse(x.q, x.k, x.cu_seqlens, wl.softmax_scale)
+    got = lse.cpu().numpy().astype(np.float64)
+    # |lse| is in the hundreds here; fp32 score sums carry ~2^-24 relative error
+    assert np.max(np.abs(got - want) / np.maximum(1.0, np.abs(want))) <= 2.0 ** -16

@@ -237,3 +237,52 @@ def test_pins_catch_planted_mistakes(monkeypatch, planted):
     monkeypatch.setattr(oattn, "segment_attention", planted)
     with pytest.raises(AssertionError):
         test_matches_torch_sdpa_float64([4, 0, 9, 1])
+
+
+# ---- log-sum-exp of the scores ----------------------------------------------
+
+def _dense_lse_scipy(q, k, cu, scale):
+    """scipy's logsumexp over each row of the block-masked score matrix."""
+    from scipy.special import logsumexp
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64)
+    T, H, _ = q.shape
+    seg = np.searchsorted(cu, np.arange(T), side="right") - 1
+    same = seg[:, None] == seg[None, :]
+    out = np.empty((T, H))
+    for h in range(H):
+        s = (q[:, h] @ k[:, h].T) * scale
+        out[:, h] = logsumexp(np.where(same, s, -np.inf), axis=1)
+    return out
+
+
+@pytest.mark.parametrize("lens", [[5, 1, 17], [30, 0, 2, 64]])
+def test_lse_matches_scipy_on_the_dense_mask(lens):
+    rng = np.random.default_rng(21)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k = (rng.standard_normal((cu[-1], 3, 16)) for _ in range(2))
+    np.testing.assert_allclose(oracle.varlen_lse(q, k, cu, 0.3), _dense_lse_scipy(q, k, cu, 0.3),
+                               rtol=1e-13, atol=1e-13)
+
+
+def test_lse_closed_forms_and_bounds():
+    rng = np.random.default_rng(22)
+    q, k = (rng.standard_normal((1, 2, 8)) for _ in range(2))
+    # one key: lse is that key's score
+    np.testing.assert_allclose(oracle.segment_lse(q, k, 0.7)[0], 0.7 * np.sum(q[0] * k[0], axis=-1),
+                               rtol=1e-14)
+    q, k = (rng.standard_normal((50, 2, 8)) for _ in range(2))
+    # scale 0: every score is 0, so lse = log(len)
+    np.testing.assert_allclose(oracle.segment_lse(q, k, 0.0), np.full((50, 2), np.log(50.0)), rtol=1e-14)
+    # max <= lse <= max + log(len), and exp(score - lse) sums to one over the keys
+    lse = oracle.segment_lse(q, k, 0.4)
+    for h in range(2):
+        s = (q[:, h] @ k[:, h].T) * 0.4
+        assert np.all(lse[:, h] >= s.max(1) - 1e-12) and np.all(lse[:, h] <= s.max(1) + np.log(50) + 1e-12)
+        np.testing.assert_allclose(np.exp(s - lse[:, h:h + 1]).sum(1), 1.0, rtol=1e-13)
+
+
+def test_lse_pins_catch_a_base_2_mistake(monkeypatch):
+    real = oracle.segment_lse
+    monkeypatch.setattr(oracle, "segment_lse", lambda q, k, scale: real(q, k, scale) / np.log(2.0))
+    with pytest.raises(AssertionError):
+        test_lse_closed_forms_and_bounds()

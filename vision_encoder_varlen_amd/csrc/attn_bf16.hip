@@ -67,6 +67,7 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) const u16 lds_u16_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRestartLimit = 0x1p64f;  // a row sum above this triggers the exact-max repeat
 // Tile modes of the key loop.
 constexpr int kSetRef = 0, kPlain = 1, kMaxOnly = 2;
@@ -178,7 +179,8 @@ template <class C, bool POS_SCALE>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
-    const int32_t* __restrict__ meta, int H, float scale_log2, u16* __restrict__ out) {
+    const int32_t* __restrict__ meta, int H, float scale_log2, u16* __restrict__ out,
+    float* __restrict__ lse) {
   constexpr int D = C::D, BN = C::BN, KB = C::KB, STAGES = C::STAGES, NI = C::NI_HI, QB = C::QB;
   // When D is not a multiple of 32 the last 32-row block of O^T has padding
   // rows; row D then collects the row sums of P (see the tile loop), and
@@ -469,6 +471,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     for (int b = 0; b < QB; ++b) {
       const int row = row0 + 32 * b + l32;
       const float l_tot = row_total(b);
+      // Log-sum-exp of the row's scores, natural log: p = 2^(x - m_ref) with
+      // x = scale * log2(e) * score, so sum_b e^(scale*score) = 2^m_ref * l.
+      if (lse != nullptr && row < len)
+        lse[size_t(start + row) * H + h] = (m_ref[b] + log2f(l_tot)) * kLn2;
       if (row < len) {
         const float inv = 1.f / l_tot;
         u16* op = out + size_t(start + row) * tok_stride + size_t(h) * D;
@@ -493,8 +499,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
 template <class C>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, const int32_t* cu,
                       const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
-                      void* out, hipStream_t stream, hipEvent_t e0,
-                    hipEvent_t e1) {
+                      void* out, float* lse, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const int64_t units = cap * int64_t(H);
   if (units <= 0) return hipSuccess;
   const int64_t grid = units < kMaxAttnGrid ? units : kMaxAttnGrid;
@@ -502,7 +507,7 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const int32_t
   auto kern = c > 0.f ? attn_bf16_kernel<C, true> : attn_bf16_kernel<C, false>;
   hipExtLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), 0, stream, e0, e1, 0,
                      static_cast<const u16*>(q), static_cast<const u16*>(k),
-                     static_cast<const u16*>(v), cu, items, meta, H, c, static_cast<u16*>(out));
+                     static_cast<const u16*>(v), cu, items, meta, H, c, static_cast<u16*>(out), lse);
   return hipGetLastError();
 }
 
@@ -518,25 +523,24 @@ template <> struct Choice<128> { using C = Cfg<128, 4, 1, 32, 2, 2>; };
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* cu,
                     const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
-                    void* out, hipStream_t stream, hipEvent_t e0,
-                    hipEvent_t e1) {
+                    void* out, float* lse, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   using C = typename Choice<D>::C;
   static_assert(C::BM == bf16_block_m_const(D), "work-list block size mismatch");
-  return launch_cfg<C>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
+  return launch_cfg<C>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const int32_t* cu,
                             const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                            float scale, void* out, hipStream_t stream, hipEvent_t e0,
-                            hipEvent_t e1) {
+                            float scale, void* out, float* lse, hipStream_t stream,
+                            hipEvent_t e0, hipEvent_t e1) {
   switch (D) {
-    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
-    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
-    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
-    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
-    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
+    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
+    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
+    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
+    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
+    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

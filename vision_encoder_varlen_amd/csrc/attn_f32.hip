@@ -29,7 +29,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
-    const int32_t* __restrict__ meta, int H, float scale, float* __restrict__ out) {
+    const int32_t* __restrict__ meta, int H, float scale, float* __restrict__ out,
+    float* __restrict__ lse) {
   constexpr int HD = D / 2;
   constexpr int ROW = D + 4;  // +16 bytes per LDS row
   __shared__ __align__(16) float ks[kBN * ROW];
@@ -100,6 +101,8 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
     }
 
     if (qrow < len) {
+      // Log-sum-exp of the row's scores (natural log): sum_b e^score = e^m * l.
+      if (lse != nullptr && half == 0) lse[size_t(start + qrow) * H + h] = m + logf(l);
       const float inv = 1.f / l;
       float* op = out + size_t(start + qrow) * tok_stride + size_t(h) * D + half * HD;
 #pragma unroll
@@ -113,15 +116,14 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* cu,
                     const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
-                    void* out, hipStream_t stream, hipEvent_t e0,
-                    hipEvent_t e1) {
+                    void* out, float* lse, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const int64_t units = cap * int64_t(H);
   if (units <= 0) return hipSuccess;
   const int64_t grid = units < kMaxAttnGrid ? units : kMaxAttnGrid;
   hipExtLaunchKernelGGL(attn_f32_kernel<D>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, e0, e1, 0,
                      static_cast<const float*>(q), static_cast<const float*>(k),
                      static_cast<const float*>(v), cu, items, meta, H, scale,
-                     static_cast<float*>(out));
+                     static_cast<float*>(out), lse);
   return hipGetLastError();
 }
 
@@ -129,14 +131,14 @@ hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* 
 
 hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu,
                            const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                           float scale, void* out, hipStream_t stream, hipEvent_t e0,
-                            hipEvent_t e1) {
+                           float scale, void* out, float* lse, hipStream_t stream,
+                           hipEvent_t e0, hipEvent_t e1) {
   switch (D) {
-    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
-    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
-    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
-    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
-    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, stream, e0, e1);
+    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
+    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
+    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
+    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
+    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

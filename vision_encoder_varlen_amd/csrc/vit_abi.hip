@@ -123,15 +123,26 @@ int check_attn_args(const void* q, const void* k, const void* v, const int32_t* 
   return VIT_OK;
 }
 
+int check_lse(const float* lse, const void* q, const void* k, const void* v, const void* out) {
+  if (lse == nullptr) return VIT_OK;
+  if (!aligned4(lse)) return fail(VIT_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (static_cast<const void*>(lse) == q || static_cast<const void*>(lse) == k ||
+      static_cast<const void*>(lse) == v || static_cast<const void*>(lse) == out)
+    return fail(VIT_ERR_INVALID_ARG, "lse must not alias q, k, v or out");
+  return VIT_OK;
+}
+
 int block_m_for(int dtype, int D) {
   return dtype == VIT_BF16 ? vit::bf16_block_m_const(D) : vit::kBlockMF32;
 }
 
 int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, int num_seqs,
-                int max_seqlen, int H, int D, float scale, void* out, hipStream_t stream,
-                int dtype) {
+                int max_seqlen, int H, int D, float scale, void* out, float* lse,
+                hipStream_t stream, int dtype) {
   const TimingHook t = take_timing();
   int rc = check_attn_args(q, k, v, cu, num_seqs, max_seqlen, H, D, scale, out);
+  if (rc != VIT_OK) return rc;
+  rc = check_lse(lse, q, k, v, out);
   if (rc != VIT_OK) return rc;
   if (int64_t(max_seqlen) * H * D * 2 > vit::kMaxSegmentBytes)
     return fail(VIT_ERR_UNSUPPORTED, "max_seqlen * num_heads * head_dim * 2 bytes exceeds %lld",
@@ -152,8 +163,8 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, 
                                       nullptr, nullptr);
   if (e != hipSuccess) return hip_fail(e, "work-list launch");
   e = dtype == VIT_BF16
-          ? vit::launch_attn_bf16(q, k, v, cu, items, cap, meta, H, D, scale, out, stream, t.start, t.stop)
-          : vit::launch_attn_f32(q, k, v, cu, items, cap, meta, H, D, scale, out, stream, t.start, t.stop);
+          ? vit::launch_attn_bf16(q, k, v, cu, items, cap, meta, H, D, scale, out, lse, stream, t.start, t.stop)
+          : vit::launch_attn_f32(q, k, v, cu, items, cap, meta, H, D, scale, out, lse, stream, t.start, t.stop);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
 }
@@ -255,14 +266,22 @@ int vit_varlen_attn(const void* q, const void* k, const void* v, const int32_t* 
                     int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
                     void* out, hipStream_t stream) {
   return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, out,
-                     stream, VIT_BF16);
+                     nullptr, stream, VIT_BF16);
 }
 
 int vit_varlen_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                         int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
                         void* out, hipStream_t stream) {
   return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, out,
-                     stream, VIT_F32);
+                     nullptr, stream, VIT_F32);
+}
+
+int vit_varlen_attn_lse(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                        int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
+                        int dtype, void* out, float* lse, hipStream_t stream) {
+  if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, out,
+                     lse, stream, dtype);
 }
 
 int vit_attn_block_m(int num_heads, int head_dim, int dtype) {
@@ -292,22 +311,24 @@ int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
 int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
                             const int32_t* cu_seqlens, const int32_t* items, int64_t cap,
                             const int32_t* meta, int num_heads, int head_dim, float scale,
-                            int dtype, void* out, hipStream_t stream) {
+                            int dtype, void* out, float* lse, hipStream_t stream) {
   const TimingHook t = take_timing();
   if (!items || !meta) return fail(VIT_ERR_INVALID_ARG, "null work-list pointer");
   if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   int rc = check_attn_args(q, k, v, cu_seqlens, 0, 0, num_heads, head_dim, scale, out);
   if (rc != VIT_OK) return rc;
   if (cap < 0 || cap > kMaxCapacity) return fail(VIT_ERR_INVALID_ARG, "bad work-list capacity %lld", (long long)cap);
+  rc = check_lse(lse, q, k, v, out);
+  if (rc != VIT_OK) return rc;
   if (cap == 0) {
     const hipError_t e = record_empty(t, stream);
     return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
   }
   hipError_t e = dtype == VIT_BF16
       ? vit::launch_attn_bf16(q, k, v, cu_seqlens, items, cap, meta, num_heads, head_dim, scale,
-                              out, stream, t.start, t.stop)
+                              out, lse, stream, t.start, t.stop)
       : vit::launch_attn_f32(q, k, v, cu_seqlens, items, cap, meta, num_heads, head_dim, scale,
-                             out, stream, t.start, t.stop);
+                             out, lse, stream, t.start, t.stop);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
 }

@@ -63,14 +63,16 @@ hipError_t launch_worklist(const int32_t* cu, int N, int max_seqlen, int block_m
 
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const int32_t* cu,
                             const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                            float scale, void* out, hipStream_t stream, hipEvent_t ev_start,
-                            hipEvent_t ev_stop);
+                            float scale, void* out, float* lse, hipStream_t stream,
+                            hipEvent_t ev_start, hipEvent_t ev_stop);
 
 hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu,
                            const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                           float scale, void* out, hipStream_t stream, hipEvent_t ev_start,
-                           hipEvent_t ev_stop);
+                           float scale, void* out, float* lse, hipStream_t stream,
+                           hipEvent_t ev_start, hipEvent_t ev_stop);
 
+// Attention launches: lse (fp32 [T, H], may be null) receives each row's
+// log-sum-exp of scores, natural log.
 // MFMA rate probe: workgroups of kProbeThreads threads, each lane reading 256
 // operand bytes from slice blockIdx % kProbeSlices (kProbeOperandBytes in
 // all); each wave issues 32 * iters MFMAs of 32x32x16.

@@ -100,11 +100,12 @@ def _attn_checks(q, k, v, cu_seqlens):
 
 def varlen_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                 max_seqlen: int, scale: Optional[float] = None,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Block-diagonal non-causal attention over packed ``[T, H, D]`` tensors.
 
     ``scale`` defaults to ``head_dim ** -0.5``.  Dispatches on dtype: bf16 uses
-    the MFMA kernel, fp32 the fp32 kernel.  Returns ``out``.
+    the MFMA kernel, fp32 the fp32 kernel.  ``lse`` (optional, fp32 ``[T, H]``)
+    receives each row's log-sum-exp of scores.  Returns ``out``.
     """
     _attn_checks(q, k, v, cu_seqlens)
     T, H, D = q.shape
@@ -116,7 +117,17 @@ def varlen_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: t
         _need_cuda("out", out, q.dtype)
         if out.shape != q.shape:
             raise ValueError("out must have the shape of q")
+    if lse is not None:
+        _need_cuda("lse", lse, torch.float32)
+        if lse.shape != (T, H):
+            raise ValueError("lse must be float32 [T, H]")
     lib = _lib.load()
+    if lse is not None:
+        _lib.check(lib.vit_varlen_attn_lse(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+            int(max_seqlen), H, D, float(scale), dtype_code(q.dtype), out.data_ptr(), lse.data_ptr(),
+            _stream(q)))
+        return out
     fn = lib.vit_varlen_attn if q.dtype == torch.bfloat16 else lib.vit_varlen_attn_f32
     dtype_code(q.dtype)
     _lib.check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
@@ -176,7 +187,8 @@ def rebuild_worklist(plan: Plan, cu_seqlens: torch.Tensor) -> Plan:
 
 def varlen_attn_planned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                         cu_seqlens: torch.Tensor, plan: Plan, scale: Optional[float] = None,
-                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                        out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Attention over a work-list from ``varlen_worklist`` (built with ``attn_block_m``)."""
     _attn_checks(q, k, v, cu_seqlens)
     T, H, D = q.shape
@@ -188,10 +200,14 @@ def varlen_attn_planned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         out = torch.empty_like(q)
     else:
         _need_cuda("out", out, q.dtype)
+    if lse is not None:
+        _need_cuda("lse", lse, torch.float32)
+        if lse.shape != (T, H):
+            raise ValueError("lse must be float32 [T, H]")
     _lib.check(_lib.load().vit_varlen_attn_planned(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), plan.items.data_ptr(),
         plan.cap, plan.meta.data_ptr(), H, D, float(scale), dtype_code(q.dtype), out.data_ptr(),
-        _stream(q)))
+        _ptr(lse), _stream(q)))
     return out
 
 

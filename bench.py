@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=2, help="seeded workload 1..5 (default 2)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--packed-qkv", action="store_true",
+                   help="read q, k, v as views of one packed [T, 3, H, D] buffer (token stride 3*H*D)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU-oracle time budget")
     p.add_argument("--traffic-json", default="",
@@ -174,13 +176,23 @@ def main():
     wl = W.config(args.config)
     x = W.generate(wl)
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    q, k, v = (torch.from_numpy(a).to(tdt).to(dev) for a in (x.q, x.k, x.v))
+    if args.packed_qkv:
+        # q, k, v as views of one packed [T, 3, H, D] projection output.
+        qkv = torch.from_numpy(np.stack([x.q, x.k, x.v], axis=1)).to(tdt).to(dev)
+        q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    else:
+        q, k, v = (torch.from_numpy(a).to(tdt).to(dev) for a in (x.q, x.k, x.v))
     pos = torch.from_numpy(x.pos).to(dev)
     cu = torch.from_numpy(x.cu_seqlens).to(dev)
     wq = torch.from_numpy(x.wq).to(dev) if wl.use_norm else None
     wk = torch.from_numpy(x.wk).to(dev) if wl.use_norm else None
-    out = torch.empty_like(q)
+    out = torch.empty(q.shape, dtype=tdt, device=dev)
     T, H, D = q.shape
+    # Token strides (elements) of q, k, v, out; None = contiguous [T, H, D].
+    strides_arr = None
+    if args.packed_qkv:
+        import ctypes
+        strides_arr = (ctypes.c_int64 * 4)(q.stride(0), k.stride(0), v.stride(0), H * D)
     dcode = ops.dtype_code(tdt)
     bm = ops.attn_block_m(H, D, tdt)
     plan = ops.varlen_worklist(cu, wl.max_seqlen, bm)
@@ -192,19 +204,19 @@ def main():
     # Precomputed ctypes arguments keep host overhead per step far below GPU time.
     pre_args = (q.data_ptr(), k.data_ptr(), T, H, D, dcode, pos.data_ptr(), float(wl.theta),
                 wq.data_ptr() if wq is not None else None, wk.data_ptr() if wk is not None else None,
-                float(wl.eps), sh)
+                float(wl.eps), strides_arr, sh)
     wl_args = (cu.data_ptr(), wl.num_seqs, wl.max_seqlen, bm, plan.items.data_ptr(), plan.cap,
                plan.meta.data_ptr(), sh)
     at_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), cu.data_ptr(), plan.items.data_ptr(),
                plan.cap, plan.meta.data_ptr(), H, D, float(wl.softmax_scale), dcode,
-               out.data_ptr(), None, sh)
+               out.data_ptr(), None, strides_arr, sh)
     # The same attention call that also writes the log-sum-exp rows (timed
     # outside the timed loop, for its overhead).
     lse_buf = torch.empty((T, H), dtype=torch.float32, device=dev)
-    at_lse_args = at_args[:-2] + (lse_buf.data_ptr(), sh)
+    at_lse_args = at_args[:-3] + (lse_buf.data_ptr(), strides_arr, sh)
     # The step's first launch: pre-pass and work-list build together.
     fused_args = pre_args[:-1] + wl_args
-    f_pre, f_wl, f_at = lib.vit_qk_norm_rope, lib.vit_varlen_worklist, lib.vit_varlen_attn_planned
+    f_pre, f_wl, f_at = lib.vit_qk_norm_rope_strided, lib.vit_varlen_worklist, lib.vit_varlen_attn_planned
     f_fused = lib.vit_qk_norm_rope_worklist
 
     if args.copy_calibration > 0:
@@ -312,7 +324,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if is_bf16 else "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "images": wl.num_seqs, "tokens": T, "heads": H,
+        "config": {"workload": wl.name + ("_packed_qkv" if args.packed_qkv else ""),
+                   "images": wl.num_seqs, "tokens": T, "heads": H,
                    "head_dim": D, "max_seqlen": wl.max_seqlen, "qk_norm": wl.use_norm,
                    "rope": "2d", "flops_per_step": flops, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma" if is_bf16 else "alu", "kernel": "attn_bf16" if is_bf16 else "attn_f32",

@@ -91,7 +91,27 @@ int vit_qk_norm_rope(void* q, void* k, int64_t total_tokens, int num_heads, int 
                      const float* k_weight, float eps, hipStream_t stream);
 
 /*
- * vit_qk_norm_rope followed by vit_varlen_worklist, in one kernel launch: the
+ * Token strides.  The strided entry points below take `strides`, an int64
+ * array of elements between consecutive tokens of each tensor (in the order
+ * the call names: q, k for the pre-pass; q, k, v, out for attention), or
+ * null for contiguous [T, H, D] (H * D).  Within a token the H head rows stay
+ * contiguous (head h at offset h * D).  This reads q, k and v straight out of
+ * a packed [T, 3, H, D] QKV projection (stride 3 * H * D; the views both
+ * pages take: reshape(seq, 3, H, D) / unbind in _VisionAttentionBase on the
+ * vLLM page, qkv.split along the last dim in MultimodalEncoderAttention on
+ * the tokenspeed page) and writes out into a wider [T, >= H * D] buffer.
+ * Each stride must be >= H * D, < 2^26, and keep rows 16-byte aligned (a
+ * multiple of 8 elements for bf16, 4 for fp32); VIT_ERR_INVALID_ARG otherwise.
+ */
+
+/* vit_qk_norm_rope on strided q and k (strides[0], strides[1]). */
+int vit_qk_norm_rope_strided(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
+                             int dtype, const int32_t* pos, float theta, const float* q_weight,
+                             const float* k_weight, float eps, const int64_t* strides,
+                             hipStream_t stream);
+
+/*
+ * vit_qk_norm_rope_strided followed by vit_varlen_worklist, in one kernel launch: the
  * two are independent, so one extra workgroup of the pre-pass launch builds
  * the work-list while the others normalise and rotate q and k.  Arguments,
  * results and errors are exactly those of the two calls (checked before
@@ -101,9 +121,9 @@ int vit_qk_norm_rope(void* q, void* k, int64_t total_tokens, int num_heads, int 
  */
 int vit_qk_norm_rope_worklist(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
                               int dtype, const int32_t* pos, float theta, const float* q_weight,
-                              const float* k_weight, float eps, const int32_t* cu_seqlens,
-                              int num_seqs, int max_seqlen, int block_m, int32_t* items,
-                              int64_t cap, int32_t* meta, hipStream_t stream);
+                              const float* k_weight, float eps, const int64_t* strides,
+                              const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int block_m,
+                              int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream);
 
 /*
  * Varlen attention, bf16 in and out, fp32 accumulation and softmax.
@@ -122,6 +142,9 @@ int vit_qk_norm_rope_worklist(void* q, void* k, int64_t total_tokens, int num_he
  *                caller so no device-to-host sync is needed (the capture-safe
  *                path of _varlen_metadata on the tokenspeed page); longer
  *                segments are skipped and flagged (VIT_WL_ERR_TOO_LONG).
+ *                (max_seqlen + 64) * token stride * 2 must not exceed 2^30
+ *                bytes, the span the kernel addresses with 32-bit buffer
+ *                offsets (VIT_ERR_UNSUPPORTED otherwise).
  *  head_dim      one of 32, 64, 80, 96, 128.
  *  out           bf16 [T, H, D]; must not alias q, k or v.  Rows of skipped
  *                segments are left untouched.
@@ -154,6 +177,12 @@ int vit_varlen_attn_lse(const void* q, const void* k, const void* v, const int32
                         int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
                         int dtype, void* out, float* lse, hipStream_t stream);
 
+/* vit_varlen_attn_lse on strided q, k, v and out (strides[0..3]; see above). */
+int vit_varlen_attn_strided(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                            int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
+                            int dtype, void* out, float* lse, const int64_t* strides,
+                            hipStream_t stream);
+
 /*
  * Query rows per (segment, q-tile) work item of the attention kernel for this
  * shape and dtype, or a negative VIT_ERR_* code for an unsupported shape.
@@ -184,13 +213,18 @@ int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
  * block_m = vit_attn_block_m(num_heads, head_dim, dtype) for the same
  * cu_seqlens.  Lets one list serve every layer of an encoder tower.
  * dtype selects the bf16 (VIT_BF16) or fp32 (VIT_F32) kernel; lse is as for
- * vit_varlen_attn_lse (null: not written); cap is the capacity the list was
- * built with; the other arguments are those of vit_varlen_attn.
+ * vit_varlen_attn_lse (null: not written); strides as for
+ * vit_varlen_attn_strided (null: contiguous); cap is the capacity the list
+ * was built with; the other arguments are those of vit_varlen_attn.  The
+ * list's max_seqlen must satisfy the bound vit_varlen_attn checks: the bf16
+ * kernel skips a segment beyond the 32-bit offset span (this call cannot see
+ * max_seqlen, so it is not rejected here).
  */
 int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
                             const int32_t* cu_seqlens, const int32_t* items, int64_t cap,
                             const int32_t* meta, int num_heads, int head_dim, float scale,
-                            int dtype, void* out, float* lse, hipStream_t stream);
+                            int dtype, void* out, float* lse, const int64_t* strides,
+                            hipStream_t stream);
 
 /*
  * Reads (and with reset != 0 clears) the work-list error bits (enum

@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
                      "vit_varlen_worklist", "vit_varlen_attn_planned", "vit_attn_block_m",
                      "vit_worklist_capacity", "vit_device_error", "vit_last_error", "vit_release",
                      "vit_time_next_kernel", "vit_probe_mfma", "vit_qk_norm_rope_worklist",
-                     "vit_varlen_attn_lse"):
+                     "vit_varlen_attn_lse", "vit_varlen_attn_strided",
+                     "vit_qk_norm_rope_strided"):
         assert required in names
     assert sorted(_lib.SIGNATURES) == names
 
@@ -114,15 +115,15 @@ def test_worklist_argument_errors(lib):
 
 def test_planned_argument_errors(lib):
     f = lib.vit_varlen_attn_planned
-    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None, None) == 1
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 5, FAKE + 0x100, None, None) == 1
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None, None, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 5, FAKE + 0x100, None, None, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None, None, None) == 1
     # lse must be aligned and must not alias the tensors
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, FAKE + 2, None) == 1
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, FAKE + 0x100, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, FAKE + 2, None, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, FAKE + 0x100, None, None) == 1
     assert "alias" in _err(lib)
     # an empty plan is a no-op
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None, None) == 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None, None, None) == 0
 
 
 def test_empty_batch_is_a_no_op(lib):
@@ -162,7 +163,7 @@ def test_probe_argument_errors(lib):
 def test_fused_prepass_worklist_checks_both_argument_sets(lib):
     f = lib.vit_qk_norm_rope_worklist
     meta = FAKE + 0x40
-    ok_pre = (FAKE, FAKE + 0x1000, 16, 2, 64, 1, None, 1e4, None, None, 1e-6)
+    ok_pre = (FAKE, FAKE + 0x1000, 16, 2, 64, 1, None, 1e4, None, None, 1e-6, None)
     ok_wl = (FAKE, 3, 10, 64, FAKE, 3, meta, None)
     assert f(None, *ok_pre[1:], *ok_wl) == _lib.VIT_ERR_INVALID_ARG          # pre-pass check
     assert "q or k" in _err(lib)
@@ -171,3 +172,42 @@ def test_fused_prepass_worklist_checks_both_argument_sets(lib):
     assert f(*ok_pre, FAKE, 3, 200, 64, FAKE, 3, meta, None) == _lib.VIT_ERR_INVALID_ARG  # capacity
     assert "capacity" in _err(lib)
     assert f(*ok_pre, FAKE, 9000, 10, 64, FAKE, 9000, meta, None) == _lib.VIT_ERR_UNSUPPORTED
+
+
+def _i64(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+def test_token_stride_errors(lib):
+    """Strides below H * D, not a whole number of 16-byte units, or >= 2^26 are rejected."""
+    f = lib.vit_varlen_attn_strided
+    base = (FAKE, FAKE + 0x100, FAKE + 0x200, FAKE, 1, 8, 2, 64, 0.125)
+    out = FAKE + 0x1000
+    for dtype, bad in ((1, (100, 128, 128, 128)),       # below H * D = 128
+                       (1, (132, 128, 128, 128)),       # bf16: 132 elements is not 16-byte units
+                       (0, (128, 130, 128, 128)),       # f32: 130 elements is not 16-byte units
+                       (1, (128, 128, 128, 1 << 26))):  # too large
+        assert f(*base, dtype, out, None, _i64(*bad), None) == _lib.VIT_ERR_INVALID_ARG
+        assert "token stride" in _err(lib)
+    # packed [T, 3, H, D]: stride 3 * H * D on q, k, v and a dense output -> valid (empty batch)
+    assert f(FAKE, FAKE + 0x100, FAKE + 0x200, FAKE, 0, 0, 2, 64, 0.125, 1, out, None,
+             _i64(384, 384, 384, 128), None) == _lib.VIT_OK
+    # a segment that would not fit the 32-bit buffer range at this stride is unsupported
+    assert f(*base[:5], 1 << 16, 2, 64, 0.125, 1, out, None, _i64(8208, 8208, 8208, 128),
+             None) == _lib.VIT_ERR_UNSUPPORTED
+    # the bound counts the last tile's key padding: (max_seqlen + 64) * stride * 2 <= 2^30
+    assert f(*base[:5], (1 << 16) - 63, 2, 64, 0.125, 1, out, None,
+             _i64(8192, 8192, 8192, 128), None) == _lib.VIT_ERR_UNSUPPORTED
+    assert "max_seqlen + 64" in _err(lib)
+    p = lib.vit_qk_norm_rope_strided
+    assert p(FAKE, FAKE + 0x100, 4, 2, 64, 1, FAKE, 1e4, None, None, 1e-6, _i64(120, 128),
+             None) == _lib.VIT_ERR_INVALID_ARG
+    # no tokens: nothing to do, valid packed strides accepted without touching memory
+    assert p(FAKE, FAKE + 0x100, 0, 2, 64, 1, FAKE, 1e4, None, None, 1e-6, _i64(384, 384),
+             None) == _lib.VIT_OK
+    planned = lib.vit_varlen_attn_planned
+    assert planned(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, out, None,
+                   _i64(128, 64, 128, 128), None) == _lib.VIT_ERR_INVALID_ARG
+    fused = lib.vit_qk_norm_rope_worklist
+    assert fused(FAKE, FAKE + 0x1000, 16, 2, 64, 1, None, 1e4, None, None, 1e-6, _i64(128, 8),
+                 FAKE, 3, 10, 64, FAKE, 3, FAKE + 0x40, None) == _lib.VIT_ERR_INVALID_ARG

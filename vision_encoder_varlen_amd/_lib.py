@@ -26,14 +26,16 @@ _I64 = ctypes.c_int64
 _F = ctypes.c_float
 SIGNATURES = {
     "vit_qk_norm_rope": (_I, [_P, _P, _I64, _I, _I, _I, _P, _F, _P, _P, _F, _P]),
-    "vit_qk_norm_rope_worklist": (_I, [_P, _P, _I64, _I, _I, _I, _P, _F, _P, _P, _F,
+    "vit_qk_norm_rope_strided": (_I, [_P, _P, _I64, _I, _I, _I, _P, _F, _P, _P, _F, _P, _P]),
+    "vit_qk_norm_rope_worklist": (_I, [_P, _P, _I64, _I, _I, _I, _P, _F, _P, _P, _F, _P,
                                        _P, _I, _I, _I, _P, _I64, _P, _P]),
     "vit_varlen_attn": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P]),
     "vit_varlen_attn_f32": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P]),
     "vit_attn_block_m": (_I, [_I, _I, _I]),
     "vit_worklist_capacity": (_I64, [_I, _I, _I]),
     "vit_varlen_worklist": (_I, [_P, _I, _I, _I, _P, _I64, _P, _P]),
-    "vit_varlen_attn_planned": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _I, _F, _I, _P, _P, _P]),
+    "vit_varlen_attn_planned": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _I, _F, _I, _P, _P, _P, _P]),
+    "vit_varlen_attn_strided": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),
     "vit_varlen_attn_lse": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P]),
     "vit_device_error": (_I, [_P, ctypes.POINTER(ctypes.c_int32), _I]),
     "vit_time_next_kernel": (_I, [_P, _P]),

@@ -76,6 +76,7 @@ constexpr int kRsrcWord3 = 0x00020000;    // gfx9-family buffer descriptor word 
 // (segments are limited to kMaxSegmentBytes) even after adding the tile offset.
 constexpr unsigned kPadOffset = 0x40000000u;
 static_assert(kMaxSegmentBytes <= (int64_t)kPadOffset, "pad offset must exceed every segment");
+static_assert((int64_t)kPadOffset + kMaxSegmentBytes < (int64_t(1) << 32), "offsets must not wrap");
 
 constexpr int odd_units(int u) { return (u & 1) ? u : u + 1; }
 constexpr int units_4_mod_8(int u) { return u % 8 == 4 ? u : units_4_mod_8(u + 1); }
@@ -112,6 +113,7 @@ struct Cfg {
   static constexpr int LDS_BYTES = STAGES * STAGE_UNITS * 16;
   static_assert(D % 16 == 0, "head dim must be a multiple of 16");
   static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
+  static_assert(BN <= kMaxKeyTile, "key tile exceeds the padding the segment limit allows for");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
   static_assert(NI_HI * (STAGES - 2) <= 63, "vmcnt range");
   static_assert(LDS_BYTES * OCC <= 160 * 1024, "LDS budget");
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
     const int32_t* __restrict__ meta, int H, float scale_log2, u16* __restrict__ out,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, TokenStrides ts) {
   constexpr int D = C::D, BN = C::BN, KB = C::KB, STAGES = C::STAGES, NI = C::NI_HI, QB = C::QB;
   // When D is not a multiple of 32 the last 32-row block of O^T has padding
   // rows; row D then collects the row sums of P (see the tile loop), and
@@ -194,7 +196,6 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31;
   const int half = lane >> 5;
-  const int tok_stride = H * D;  // elements per token
   const unsigned smem_base = static_cast<unsigned>((uintptr_t)(lds_u16_t*)smem);  // LDS address
 
   // Per-lane byte offsets of this wave's copy instructions relative to the
@@ -215,7 +216,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     const int col = u - row * str;
     const int key = is_k ? swap_bits_2_3(row) : row;
     const bool data = row < BN && col < C::DU;
-    cp_off[j] = data ? unsigned((key * tok_stride + col * 8) * 2) : kPadOffset;
+    cp_off[j] = data ? (unsigned(key) * unsigned(is_k ? ts.k : ts.v) + unsigned(col) * 8u) * 2u
+                     : kPadOffset;
     cp_is_k[j] = is_k;
     cp_lds[j] = unsigned((is_k ? i * 64 : C::KREG + (i - C::NK) * 64) * 16);
   }
@@ -233,13 +235,16 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     const int start = cu[seg];
     const int len = cu[seg + 1] - start;
     // Offsets are 32-bit: a segment larger than the addressable span is skipped
-    // (the host rejects the max_seqlen that would allow it).
-    if (int64_t(len) * tok_stride * 2 > kMaxSegmentBytes) continue;
+    // (the host rejects the max_seqlen that would allow it).  Within the span,
+    // every copy offset, padding rows of the last tile included, stays below
+    // kPadOffset + kMaxSegmentBytes < 2^32.
+    if (!segment_fits(len, ts.k > ts.v ? ts.k : ts.v)) continue;
     const int row0 = qt * C::BM + wave * 32 * QB;  // first query row of this wave
     const bool wave_active = row0 < len;
-    const unsigned seg_bytes = unsigned(((len - 1) * tok_stride + D) * 2);
-    const i32x4_t krs = make_rsrc(k + size_t(start) * tok_stride + size_t(h) * D, seg_bytes);
-    const i32x4_t vrs = make_rsrc(v + size_t(start) * tok_stride + size_t(h) * D, seg_bytes);
+    const i32x4_t krs = make_rsrc(k + size_t(start) * ts.k + size_t(h) * D,
+                                  unsigned(((len - 1) * ts.k + D) * 2));
+    const i32x4_t vrs = make_rsrc(v + size_t(start) * ts.v + size_t(h) * D,
+                                  unsigned(((len - 1) * ts.v + D) * 2));
 
     // Q^T fragments (B operand of S^T = K Q^T): lane holds 8 dims of its row
     // in each of the wave's QB query blocks.
@@ -248,7 +253,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     for (int b = 0; b < QB; ++b) {
       const int row = row0 + 32 * b + l32;
       if (row < len) {
-        const u16* qp = q + size_t(start + row) * tok_stride + size_t(h) * D + half * 8;
+        const u16* qp = q + size_t(start + row) * ts.q + size_t(h) * D + half * 8;
 #pragma unroll
         for (int st = 0; st < C::KSTEPS; ++st)
           qf[b][st] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qp + st * 16));
@@ -273,12 +278,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     float l_run[QB];
     const int ntiles = (len + BN - 1) / BN;
     auto issue_tile = [&](int t) {
-      const unsigned tile_off = unsigned(t) * unsigned(BN * 2) * unsigned(tok_stride);
+      const unsigned tile_off_k = unsigned(t) * unsigned(BN * 2) * unsigned(ts.k);
+      const unsigned tile_off_v = unsigned(t) * unsigned(BN * 2) * unsigned(ts.v);
       const unsigned stage_lds = smem_base + unsigned((t % STAGES) * C::STAGE_UNITS * 16);
 #pragma unroll
       for (int j = 0; j < NI; ++j)
         if (j < C::NI_LO || wave_hi)
-          copy_to_lds(stage_lds + cp_lds[j], cp_off[j] + tile_off, cp_is_k[j] ? krs : vrs);
+          copy_to_lds(stage_lds + cp_lds[j], cp_off[j] + (cp_is_k[j] ? tile_off_k : tile_off_v),
+                      cp_is_k[j] ? krs : vrs);
     };
     // Sum of p over the whole row b (both lane halves).
     auto row_total = [&](int b) {
@@ -477,7 +484,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
         lse[size_t(start + row) * H + h] = (m_ref[b] + log2f(l_tot)) * kLn2;
       if (row < len) {
         const float inv = 1.f / l_tot;
-        u16* op = out + size_t(start + row) * tok_stride + size_t(h) * D;
+        u16* op = out + size_t(start + row) * ts.o + size_t(h) * D;
 #pragma unroll
         for (int d = 0; d < C::DB; ++d) {
 #pragma unroll
@@ -499,7 +506,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
 template <class C>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, const int32_t* cu,
                       const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
-                      void* out, float* lse, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+                      void* out, float* lse, TokenStrides ts, hipStream_t stream, hipEvent_t e0,
+                      hipEvent_t e1) {
   const int64_t units = cap * int64_t(H);
   if (units <= 0) return hipSuccess;
   const int64_t grid = units < kMaxAttnGrid ? units : kMaxAttnGrid;
@@ -507,7 +515,7 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const int32_t
   auto kern = c > 0.f ? attn_bf16_kernel<C, true> : attn_bf16_kernel<C, false>;
   hipExtLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), 0, stream, e0, e1, 0,
                      static_cast<const u16*>(q), static_cast<const u16*>(k),
-                     static_cast<const u16*>(v), cu, items, meta, H, c, static_cast<u16*>(out), lse);
+                     static_cast<const u16*>(v), cu, items, meta, H, c, static_cast<u16*>(out), lse, ts);
   return hipGetLastError();
 }
 
@@ -523,24 +531,25 @@ template <> struct Choice<128> { using C = Cfg<128, 4, 1, 32, 2, 2>; };
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* cu,
                     const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
-                    void* out, float* lse, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+                    void* out, float* lse, TokenStrides ts, hipStream_t stream, hipEvent_t e0,
+                    hipEvent_t e1) {
   using C = typename Choice<D>::C;
   static_assert(C::BM == bf16_block_m_const(D), "work-list block size mismatch");
-  return launch_cfg<C>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
+  return launch_cfg<C>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const int32_t* cu,
                             const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                            float scale, void* out, float* lse, hipStream_t stream,
-                            hipEvent_t e0, hipEvent_t e1) {
+                            float scale, void* out, float* lse, TokenStrides ts,
+                            hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   switch (D) {
-    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
-    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
-    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
-    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
-    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
+    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
+    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
+    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
+    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
+    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

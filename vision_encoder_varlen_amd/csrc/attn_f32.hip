@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
     const int32_t* __restrict__ meta, int H, float scale, float* __restrict__ out,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, TokenStrides ts) {
   constexpr int HD = D / 2;
   constexpr int ROW = D + 4;  // +16 bytes per LDS row
   __shared__ __align__(16) float ks[kBN * ROW];
@@ -39,7 +39,6 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
   const int lane = threadIdx.x;
   const int r = lane & 31;
   const int half = lane >> 5;
-  const size_t tok_stride = size_t(H) * D;
 
   const int64_t nunits = int64_t(meta[0]) * H;
   for (int64_t unit = blockIdx.x; unit < nunits; unit += gridDim.x) {
@@ -55,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
 #pragma unroll
     for (int d = 0; d < HD; ++d) acc[d] = 0.f;
     if (qrow < len) {
-      const float* qp = q + size_t(start + qrow) * tok_stride + size_t(h) * D + half * HD;
+      const float* qp = q + size_t(start + qrow) * ts.q + size_t(h) * D + half * HD;
 #pragma unroll
       for (int d = 0; d < HD; d += 4) {
         const float4 x = *reinterpret_cast<const float4*>(qp + d);
@@ -74,9 +73,9 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
         const int dc = c - key * (D / 4);
         float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
         if (kv0 + key < len) {
-          const size_t off = size_t(start + kv0 + key) * tok_stride + size_t(h) * D + dc * 4;
-          kx = *reinterpret_cast<const float4*>(k + off);
-          vx = *reinterpret_cast<const float4*>(v + off);
+          const size_t tok = size_t(start + kv0 + key);
+          kx = *reinterpret_cast<const float4*>(k + tok * ts.k + size_t(h) * D + dc * 4);
+          vx = *reinterpret_cast<const float4*>(v + tok * ts.v + size_t(h) * D + dc * 4);
         }
         *reinterpret_cast<float4*>(ks + key * ROW + dc * 4) = kx;
         *reinterpret_cast<float4*>(vs + key * ROW + dc * 4) = vx;
@@ -104,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
       // Log-sum-exp of the row's scores (natural log): sum_b e^score = e^m * l.
       if (lse != nullptr && half == 0) lse[size_t(start + qrow) * H + h] = m + logf(l);
       const float inv = 1.f / l;
-      float* op = out + size_t(start + qrow) * tok_stride + size_t(h) * D + half * HD;
+      float* op = out + size_t(start + qrow) * ts.o + size_t(h) * D + half * HD;
 #pragma unroll
       for (int d = 0; d < HD; d += 4)
         *reinterpret_cast<float4*>(op + d) =
@@ -116,14 +115,15 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* cu,
                     const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
-                    void* out, float* lse, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+                    void* out, float* lse, TokenStrides ts, hipStream_t stream, hipEvent_t e0,
+                    hipEvent_t e1) {
   const int64_t units = cap * int64_t(H);
   if (units <= 0) return hipSuccess;
   const int64_t grid = units < kMaxAttnGrid ? units : kMaxAttnGrid;
   hipExtLaunchKernelGGL(attn_f32_kernel<D>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, e0, e1, 0,
                      static_cast<const float*>(q), static_cast<const float*>(k),
                      static_cast<const float*>(v), cu, items, meta, H, scale,
-                     static_cast<float*>(out), lse);
+                     static_cast<float*>(out), lse, ts);
   return hipGetLastError();
 }
 
@@ -131,14 +131,14 @@ hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* 
 
 hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu,
                            const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                           float scale, void* out, float* lse, hipStream_t stream,
-                           hipEvent_t e0, hipEvent_t e1) {
+                           float scale, void* out, float* lse, TokenStrides ts,
+                           hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   switch (D) {
-    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
-    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
-    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
-    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
-    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, lse, stream, e0, e1);
+    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
+    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
+    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
+    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
+    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

@@ -105,7 +105,7 @@ template <typename T, int E>
 __global__ __launch_bounds__(kThreads) void prepass_kernel(
     T* __restrict__ q, T* __restrict__ k, long long T_tok, int H, int D, int G, int tok_per_grp,
     const int32_t* __restrict__ pos, Freqs freqs, const float* __restrict__ wq,
-    const float* __restrict__ wk, float eps, WorklistJob job) {
+    const float* __restrict__ wk, float eps, WorklistJob job, int qs, int ks) {
   extern __shared__ float2 cs[];  // [tok_per_grp][D/2] (cos, sin)
   __shared__ int s_wave[kThreads / 64];
   // With a work-list job workgroup 0 (dispatched first) builds the list,
@@ -175,15 +175,16 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
       const bool row_ok = row < ntok * H && lane_active;
       const int tl = row / H;
       const int h = row - tl * H;
-      const size_t base = (size_t(t0 + tl) * H + h) * size_t(D);
+      const size_t qbase = size_t(t0 + tl) * qs + size_t(h) * D;
+      const size_t kbase = size_t(t0 + tl) * ks + size_t(h) * D;
       // Both tensors' loads are issued before any arithmetic, so each lane
       // keeps four independent loads in flight.
       float a[2][E] = {}, b[2][E] = {};
       if (row_ok) {
-        loadE<E>(q + base + m0, a[0]);
-        loadE<E>(q + base + m0 + half_d, b[0]);
-        loadE<E>(k + base + m0, a[1]);
-        loadE<E>(k + base + m0 + half_d, b[1]);
+        loadE<E>(q + qbase + m0, a[0]);
+        loadE<E>(q + qbase + m0 + half_d, b[0]);
+        loadE<E>(k + kbase + m0, a[1]);
+        loadE<E>(k + kbase + m0 + half_d, b[1]);
       }
       if (norm) {
         float ss[2];
@@ -220,10 +221,10 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
         }
       }
       if (row_ok) {
-        storeE<E>(q + base + m0, a[0]);
-        storeE<E>(q + base + m0 + half_d, b[0]);
-        storeE<E>(k + base + m0, a[1]);
-        storeE<E>(k + base + m0 + half_d, b[1]);
+        storeE<E>(q + qbase + m0, a[0]);
+        storeE<E>(q + qbase + m0 + half_d, b[0]);
+        storeE<E>(k + kbase + m0, a[1]);
+        storeE<E>(k + kbase + m0 + half_d, b[1]);
       }
     }
     if (rope) __syncthreads();  // cs is rewritten by the next token group
@@ -235,7 +236,9 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
 hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
                           const int32_t* pos, const double* inv_freq_host, const float* wq,
                           const float* wk, float eps, hipStream_t stream, hipEvent_t e0,
-                          hipEvent_t e1, const WorklistJob* job) {
+                          hipEvent_t e1, const WorklistJob* job, int q_stride, int k_stride) {
+  const int qs = q_stride > 0 ? q_stride : H * D;
+  const int ks = k_stride > 0 ? k_stride : H * D;
   WorklistJob jb{};
   if (job != nullptr) jb = *job;
   const bool prepass_work = T > 0 && (pos != nullptr || wq != nullptr);
@@ -284,15 +287,15 @@ hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
   if (dtype == 1 && E == 8) {
     hipExtLaunchKernelGGL(prepass_kernel<u16, 8>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
                           e0, e1, 0, static_cast<u16*>(q), static_cast<u16*>(k), (long long)T, H, D,
-                          G, tok_per_grp, pos, fr, wq, wk, eps, jb);
+                          G, tok_per_grp, pos, fr, wq, wk, eps, jb, qs, ks);
   } else if (dtype == 1) {
     hipExtLaunchKernelGGL(prepass_kernel<u16, 4>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
                           e0, e1, 0, static_cast<u16*>(q), static_cast<u16*>(k), (long long)T, H, D,
-                          G, tok_per_grp, pos, fr, wq, wk, eps, jb);
+                          G, tok_per_grp, pos, fr, wq, wk, eps, jb, qs, ks);
   } else {
     hipExtLaunchKernelGGL(prepass_kernel<float, 4>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
                           e0, e1, 0, static_cast<float*>(q), static_cast<float*>(k), (long long)T, H,
-                          D, G, tok_per_grp, pos, fr, wq, wk, eps, jb);
+                          D, G, tok_per_grp, pos, fr, wq, wk, eps, jb, qs, ks);
   }
   return hipGetLastError();
 }

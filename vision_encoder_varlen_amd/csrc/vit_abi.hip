@@ -123,6 +123,25 @@ int check_attn_args(const void* q, const void* k, const void* v, const int32_t* 
   return VIT_OK;
 }
 
+// Token strides (elements) of q, k, v, out from a caller array of n values
+// (null: all H * D).  Each must be >= H * D, keep rows 16-byte aligned, and
+// stay below 2^26.
+int make_strides(const int64_t* st, int n, int H, int D, int dtype, vit::TokenStrides* ts) {
+  const int64_t dense = int64_t(H) * D;
+  int64_t v[4] = {dense, dense, dense, dense};
+  if (st != nullptr)
+    for (int i = 0; i < n; ++i) v[i] = st[i];
+  const int64_t unit = dtype == VIT_BF16 ? 8 : 4;  // elements per 16 bytes
+  for (int i = 0; i < 4; ++i) {
+    if (v[i] < dense || v[i] >= (int64_t(1) << 26) || v[i] % unit != 0)
+      return fail(VIT_ERR_INVALID_ARG,
+                  "token stride %lld must be >= num_heads * head_dim (%lld), < 2^26 and a "
+                  "multiple of %lld elements", (long long)v[i], (long long)dense, (long long)unit);
+  }
+  *ts = vit::TokenStrides{int(v[0]), int(v[1]), int(v[2]), int(v[3])};
+  return VIT_OK;
+}
+
 int check_lse(const float* lse, const void* q, const void* k, const void* v, const void* out) {
   if (lse == nullptr) return VIT_OK;
   if (!aligned4(lse)) return fail(VIT_ERR_INVALID_ARG, "lse must be 4-byte aligned");
@@ -138,15 +157,18 @@ int block_m_for(int dtype, int D) {
 
 int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, int num_seqs,
                 int max_seqlen, int H, int D, float scale, void* out, float* lse,
-                hipStream_t stream, int dtype) {
+                const int64_t* strides, hipStream_t stream, int dtype) {
   const TimingHook t = take_timing();
   int rc = check_attn_args(q, k, v, cu, num_seqs, max_seqlen, H, D, scale, out);
   if (rc != VIT_OK) return rc;
   rc = check_lse(lse, q, k, v, out);
   if (rc != VIT_OK) return rc;
-  if (int64_t(max_seqlen) * H * D * 2 > vit::kMaxSegmentBytes)
-    return fail(VIT_ERR_UNSUPPORTED, "max_seqlen * num_heads * head_dim * 2 bytes exceeds %lld",
-                (long long)vit::kMaxSegmentBytes);
+  vit::TokenStrides ts{};
+  rc = make_strides(strides, 4, H, D, dtype, &ts);
+  if (rc != VIT_OK) return rc;
+  if (!vit::segment_fits(max_seqlen, ts.k > ts.v ? ts.k : ts.v))
+    return fail(VIT_ERR_UNSUPPORTED, "(max_seqlen + %d) * token stride * 2 bytes exceeds %lld",
+                vit::kMaxKeyTile, (long long)vit::kMaxSegmentBytes);
   if (num_seqs == 0 || max_seqlen == 0) {
     const hipError_t e = record_empty(t, stream);
     return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
@@ -163,8 +185,10 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, 
                                       nullptr, nullptr);
   if (e != hipSuccess) return hip_fail(e, "work-list launch");
   e = dtype == VIT_BF16
-          ? vit::launch_attn_bf16(q, k, v, cu, items, cap, meta, H, D, scale, out, lse, stream, t.start, t.stop)
-          : vit::launch_attn_f32(q, k, v, cu, items, cap, meta, H, D, scale, out, lse, stream, t.start, t.stop);
+          ? vit::launch_attn_bf16(q, k, v, cu, items, cap, meta, H, D, scale, out, lse, ts, stream,
+                                  t.start, t.stop)
+          : vit::launch_attn_f32(q, k, v, cu, items, cap, meta, H, D, scale, out, lse, ts, stream,
+                                 t.start, t.stop);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
 }
@@ -215,7 +239,7 @@ int check_worklist_args(const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
 int launch_prepass_job(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
                        int dtype, const int32_t* pos, float theta, const float* q_weight,
                        const float* k_weight, float eps, const vit::WorklistJob* job,
-                       hipStream_t stream, const TimingHook& t) {
+                       const vit::TokenStrides& ts, hipStream_t stream, const TimingHook& t) {
   const bool prepass_work = total_tokens > 0 && (pos != nullptr || q_weight != nullptr);
   if (!prepass_work && job == nullptr) {
     const hipError_t e = record_empty(t, stream);
@@ -226,7 +250,8 @@ int launch_prepass_job(void* q, void* k, int64_t total_tokens, int num_heads, in
   const int F = head_dim / 4;
   for (int j = 0; j < F; ++j) inv_freq[j] = std::pow(double(theta), -2.0 * j / (head_dim / 2.0));
   hipError_t e = vit::launch_prepass(q, k, total_tokens, num_heads, head_dim, dtype, pos, inv_freq,
-                                     q_weight, k_weight, eps, stream, t.start, t.stop, job);
+                                     q_weight, k_weight, eps, stream, t.start, t.stop, job, ts.q,
+                                     ts.k);
   if (e != hipSuccess) return hip_fail(e, job ? "pre-pass + work-list launch" : "pre-pass launch");
   return ok();
 }
@@ -238,42 +263,56 @@ extern "C" {
 int vit_qk_norm_rope(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
                      int dtype, const int32_t* pos, float theta, const float* q_weight,
                      const float* k_weight, float eps, hipStream_t stream) {
+  return vit_qk_norm_rope_strided(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta,
+                                  q_weight, k_weight, eps, nullptr, stream);
+}
+
+int vit_qk_norm_rope_strided(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
+                             int dtype, const int32_t* pos, float theta, const float* q_weight,
+                             const float* k_weight, float eps, const int64_t* strides,
+                             hipStream_t stream) {
   const TimingHook t = take_timing();
-  const int rc = check_prepass_args(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta,
-                                    q_weight, k_weight, eps);
+  int rc = check_prepass_args(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta,
+                              q_weight, k_weight, eps);
+  if (rc != VIT_OK) return rc;
+  vit::TokenStrides ts{};
+  rc = make_strides(strides, 2, num_heads, head_dim, dtype, &ts);
   if (rc != VIT_OK) return rc;
   return launch_prepass_job(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta, q_weight,
-                            k_weight, eps, nullptr, stream, t);
+                            k_weight, eps, nullptr, ts, stream, t);
 }
 
 int vit_qk_norm_rope_worklist(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
                               int dtype, const int32_t* pos, float theta, const float* q_weight,
-                              const float* k_weight, float eps, const int32_t* cu_seqlens,
-                              int num_seqs, int max_seqlen, int block_m, int32_t* items,
-                              int64_t cap, int32_t* meta, hipStream_t stream) {
+                              const float* k_weight, float eps, const int64_t* strides,
+                              const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int block_m,
+                              int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream) {
   const TimingHook t = take_timing();
   int rc = check_prepass_args(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta, q_weight,
                               k_weight, eps);
+  if (rc != VIT_OK) return rc;
+  vit::TokenStrides ts{};
+  rc = make_strides(strides, 2, num_heads, head_dim, dtype, &ts);
   if (rc != VIT_OK) return rc;
   rc = check_worklist_args(cu_seqlens, num_seqs, max_seqlen, block_m, items, cap, meta);
   if (rc != VIT_OK) return rc;
   const vit::WorklistJob job{cu_seqlens, num_seqs, 0, max_seqlen, block_m, items, cap, meta};
   return launch_prepass_job(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta, q_weight,
-                            k_weight, eps, &job, stream, t);
+                            k_weight, eps, &job, ts, stream, t);
 }
 
 int vit_varlen_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                     int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
                     void* out, hipStream_t stream) {
   return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, out,
-                     nullptr, stream, VIT_BF16);
+                     nullptr, nullptr, stream, VIT_BF16);
 }
 
 int vit_varlen_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                         int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
                         void* out, hipStream_t stream) {
   return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, out,
-                     nullptr, stream, VIT_F32);
+                     nullptr, nullptr, stream, VIT_F32);
 }
 
 int vit_varlen_attn_lse(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
@@ -281,7 +320,16 @@ int vit_varlen_attn_lse(const void* q, const void* k, const void* v, const int32
                         int dtype, void* out, float* lse, hipStream_t stream) {
   if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, out,
-                     lse, stream, dtype);
+                     lse, nullptr, stream, dtype);
+}
+
+int vit_varlen_attn_strided(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                            int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
+                            int dtype, void* out, float* lse, const int64_t* strides,
+                            hipStream_t stream) {
+  if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, out,
+                     lse, strides, stream, dtype);
 }
 
 int vit_attn_block_m(int num_heads, int head_dim, int dtype) {
@@ -311,7 +359,8 @@ int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
 int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
                             const int32_t* cu_seqlens, const int32_t* items, int64_t cap,
                             const int32_t* meta, int num_heads, int head_dim, float scale,
-                            int dtype, void* out, float* lse, hipStream_t stream) {
+                            int dtype, void* out, float* lse, const int64_t* strides,
+                            hipStream_t stream) {
   const TimingHook t = take_timing();
   if (!items || !meta) return fail(VIT_ERR_INVALID_ARG, "null work-list pointer");
   if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
@@ -320,15 +369,18 @@ int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
   if (cap < 0 || cap > kMaxCapacity) return fail(VIT_ERR_INVALID_ARG, "bad work-list capacity %lld", (long long)cap);
   rc = check_lse(lse, q, k, v, out);
   if (rc != VIT_OK) return rc;
+  vit::TokenStrides ts{};
+  rc = make_strides(strides, 4, num_heads, head_dim, dtype, &ts);
+  if (rc != VIT_OK) return rc;
   if (cap == 0) {
     const hipError_t e = record_empty(t, stream);
     return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
   }
   hipError_t e = dtype == VIT_BF16
       ? vit::launch_attn_bf16(q, k, v, cu_seqlens, items, cap, meta, num_heads, head_dim, scale,
-                              out, lse, stream, t.start, t.stop)
+                              out, lse, ts, stream, t.start, t.stop)
       : vit::launch_attn_f32(q, k, v, cu_seqlens, items, cap, meta, num_heads, head_dim, scale,
-                             out, lse, stream, t.start, t.stop);
+                             out, lse, ts, stream, t.start, t.stop);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
 }

@@ -7,6 +7,13 @@
 
 namespace vit {
 
+// Elements between consecutive tokens of each tensor ([T, H, D] contiguous:
+// H * D; a view of a packed [T, 3, H, D] projection: 3 * H * D).  Rows of one
+// token's heads stay contiguous (head h at offset h * D).
+struct TokenStrides {
+  int q, k, v, o;
+};
+
 // Every launch_* takes ev_start / ev_stop: both null, or both timing events
 // that are recorded at its kernel's dispatch start and end (hipExtLaunchKernel).
 
@@ -18,11 +25,16 @@ constexpr int kBlockMF32 = 32;  // 1 wave, lane pairs share a row, fp32 kernel
 // Work-list builder limits: one workgroup sorts every segment in LDS.
 constexpr int kWorklistMaxSeqs = 8192;
 
-// Largest span of one segment's rows in a q, k or v tensor (bytes) that the
-// bf16 attention kernel addresses with 32-bit buffer offsets.  Segments whose
-// len * H * D * 2 exceeds it are skipped by the kernel; the C ABI rejects
-// max_seqlen values that allow them.
+// Largest span of one segment's rows in a k or v tensor (bytes) that the
+// bf16 attention kernel addresses with 32-bit buffer offsets, counted with the
+// key padding of its last tile (up to kMaxKeyTile rows).  Segments that do not
+// fit are skipped by the kernel; the C ABI rejects max_seqlen values that
+// allow them.
 constexpr int64_t kMaxSegmentBytes = int64_t(1) << 30;
+constexpr int kMaxKeyTile = 64;
+inline __host__ __device__ bool segment_fits(int64_t len, int64_t token_stride) {
+  return (len + kMaxKeyTile) * token_stride * 2 <= kMaxSegmentBytes;
+}
 
 // Upper bound on attention workgroups per launch; larger work loops inside.
 constexpr int64_t kMaxAttnGrid = int64_t(1) << 22;
@@ -48,14 +60,15 @@ struct WorklistJob {
 constexpr size_t kFusedWorklistMaxLds = 24 * 1024;
 
 // Pre-pass: inv_freq_host holds the D/4 rotary inverse frequencies in double
-// (may be null when pos is null).  dtype: 0 = fp32, 1 = bf16.  With a job,
+// (may be null when pos is null).  dtype: 0 = fp32, 1 = bf16.  q_stride /
+// k_stride: elements per token (0 = H * D).  With a job,
 // the work-list is built by one more workgroup of the same launch (the two
 // are independent).
 hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
                           const int32_t* pos, const double* inv_freq_host,
                           const float* wq, const float* wk, float eps, hipStream_t stream,
                           hipEvent_t ev_start, hipEvent_t ev_stop,
-                          const WorklistJob* job = nullptr);
+                          const WorklistJob* job = nullptr, int q_stride = 0, int k_stride = 0);
 
 hipError_t launch_worklist(const int32_t* cu, int N, int max_seqlen, int block_m,
                            int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream,
@@ -63,13 +76,13 @@ hipError_t launch_worklist(const int32_t* cu, int N, int max_seqlen, int block_m
 
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const int32_t* cu,
                             const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                            float scale, void* out, float* lse, hipStream_t stream,
-                            hipEvent_t ev_start, hipEvent_t ev_stop);
+                            float scale, void* out, float* lse, TokenStrides ts,
+                            hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu,
                            const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                           float scale, void* out, float* lse, hipStream_t stream,
-                           hipEvent_t ev_start, hipEvent_t ev_stop);
+                           float scale, void* out, float* lse, TokenStrides ts,
+                           hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 // Attention launches: lse (fp32 [T, H], may be null) receives each row's
 // log-sum-exp of scores, natural log.

@@ -24,13 +24,28 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _need_cuda(name: str, t: torch.Tensor, dtype=None) -> None:
+def _need_cuda(name: str, t: torch.Tensor, dtype=None, token_strided: bool = False) -> None:
+    """CUDA tensor of ``dtype``; contiguous, or (``token_strided``) a ``[T, H, D]``
+    view whose heads are contiguous within a token (any token stride)."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a CUDA (HIP) tensor")
-    if not t.is_contiguous():
+    if token_strided and t.dim() == 3:
+        _, H, D = t.shape
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError(f"{name}: the heads of a token must be contiguous ([T, H, D] view)")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _strides(*ts: torch.Tensor):
+    """ctypes int64 array of the tensors' token strides, or None when all are dense."""
+    import ctypes
+    vals = [t.stride(0) if t.shape[0] > 1 else t.shape[1] * t.shape[2] for t in ts]
+    if all(v == t.shape[1] * t.shape[2] for v, t in zip(vals, ts)):
+        return None
+    return (ctypes.c_int64 * len(vals))(*vals)
 
 
 def dtype_code(dtype: torch.dtype) -> int:
@@ -40,8 +55,8 @@ def dtype_code(dtype: torch.dtype) -> int:
 
 
 def _prepass_checks(q, k, pos, q_weight, k_weight) -> None:
-    _need_cuda("q", q)
-    _need_cuda("k", k, q.dtype)
+    _need_cuda("q", q, token_strided=True)
+    _need_cuda("k", k, q.dtype, token_strided=True)
     if q.dim() != 3 or k.shape != q.shape:
         raise ValueError("q and k must both be [T, H, D]")
     T, H, D = q.shape
@@ -62,9 +77,9 @@ def qk_norm_rope_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch.Tensor] 
     """In-place Q/K RMSNorm (when weights are given) then 2D rotary (when ``pos`` is given)."""
     _prepass_checks(q, k, pos, q_weight, k_weight)
     T, H, D = q.shape
-    _lib.check(_lib.load().vit_qk_norm_rope(
+    _lib.check(_lib.load().vit_qk_norm_rope_strided(
         q.data_ptr(), k.data_ptr(), T, H, D, dtype_code(q.dtype), _ptr(pos), float(theta),
-        _ptr(q_weight), _ptr(k_weight), float(eps), _stream(q)))
+        _ptr(q_weight), _ptr(k_weight), float(eps), _strides(q, k), _stream(q)))
 
 
 def qk_norm_rope_worklist_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch.Tensor],
@@ -79,16 +94,16 @@ def qk_norm_rope_worklist_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch
     T, H, D = q.shape
     _lib.check(_lib.load().vit_qk_norm_rope_worklist(
         q.data_ptr(), k.data_ptr(), T, H, D, dtype_code(q.dtype), _ptr(pos), float(theta),
-        _ptr(q_weight), _ptr(k_weight), float(eps), cu_seqlens.data_ptr(), plan.num_seqs,
+        _ptr(q_weight), _ptr(k_weight), float(eps), _strides(q, k), cu_seqlens.data_ptr(), plan.num_seqs,
         plan.max_seqlen, plan.block_m, plan.items.data_ptr(), plan.cap, plan.meta.data_ptr(),
         _stream(q)))
     return plan
 
 
 def _attn_checks(q, k, v, cu_seqlens):
-    _need_cuda("q", q)
+    _need_cuda("q", q, token_strided=True)
     for name, t in (("k", k), ("v", v)):
-        _need_cuda(name, t, q.dtype)
+        _need_cuda(name, t, q.dtype, token_strided=True)
         if t.shape != q.shape:
             raise ValueError(f"{name} must have the shape of q")
     if q.dim() != 3:
@@ -114,7 +129,7 @@ def varlen_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: t
     if out is None:
         out = torch.empty_like(q)
     else:
-        _need_cuda("out", out, q.dtype)
+        _need_cuda("out", out, q.dtype, token_strided=True)
         if out.shape != q.shape:
             raise ValueError("out must have the shape of q")
     if lse is not None:
@@ -122,11 +137,12 @@ def varlen_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: t
         if lse.shape != (T, H):
             raise ValueError("lse must be float32 [T, H]")
     lib = _lib.load()
-    if lse is not None:
-        _lib.check(lib.vit_varlen_attn_lse(
+    strides = _strides(q, k, v, out)
+    if lse is not None or strides is not None:
+        _lib.check(lib.vit_varlen_attn_strided(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
-            int(max_seqlen), H, D, float(scale), dtype_code(q.dtype), out.data_ptr(), lse.data_ptr(),
-            _stream(q)))
+            int(max_seqlen), H, D, float(scale), dtype_code(q.dtype), out.data_ptr(), _ptr(lse),
+            strides, _stream(q)))
         return out
     fn = lib.vit_varlen_attn if q.dtype == torch.bfloat16 else lib.vit_varlen_attn_f32
     dtype_code(q.dtype)
@@ -199,7 +215,9 @@ def varlen_attn_planned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if out is None:
         out = torch.empty_like(q)
     else:
-        _need_cuda("out", out, q.dtype)
+        _need_cuda("out", out, q.dtype, token_strided=True)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
     if lse is not None:
         _need_cuda("lse", lse, torch.float32)
         if lse.shape != (T, H):
@@ -207,7 +225,7 @@ def varlen_attn_planned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _lib.check(_lib.load().vit_varlen_attn_planned(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), plan.items.data_ptr(),
         plan.cap, plan.meta.data_ptr(), H, D, float(scale), dtype_code(q.dtype), out.data_ptr(),
-        _ptr(lse), _stream(q)))
+        _ptr(lse), _strides(q, k, v, out), _stream(q)))
     return out
 
 

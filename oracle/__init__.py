@@ -23,21 +23,27 @@ What it computes, and what the pages say about it:
 * ``rounding`` -- storage rounding of fp64 results to bf16 / fp32.
 * ``segment_lse`` / ``varlen_lse`` -- the log-sum-exp of each row's scores
   (natural log), the optional second result of the attention.
+* variants on the pages: the ``causal`` flag of the attention functions
+  (``is_causal`` of the vLLM page), ``uniform_cu_seqlens`` /
+  ``dense_batch_attention`` (the ``cu_seqlens = None`` batch of
+  ``_varlen_metadata`` on the tokenspeed page) and ``apply_rope_2d_complex``
+  (``position_embedding_mode = "complex_rope"`` on the tokenspeed page).
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 something other than itself (an independent formulation from the pages, a
 library routine, a closed form, brute force on tiny inputs, or an invariant).
 No function is "parity unpinned".
 """
-from .attention import (segment_attention, segment_lse, varlen_attention,
-                        varlen_attention_rows, varlen_lse)
-from .prepass import (apply_rope_2d, qk_norm_rope, rms_norm, rope_angles,
-                      rope_inv_freq)
+from .attention import (dense_batch_attention, segment_attention, segment_lse,
+                        uniform_cu_seqlens, varlen_attention, varlen_attention_rows, varlen_lse)
+from .prepass import (ROPE_MODES, apply_rope_2d, apply_rope_2d_complex, qk_norm_rope, rms_norm,
+                      rope_angles, rope_inv_freq)
 from .rounding import round_to_bf16, round_to_f32, round_to_dtype
 from .worklist import worklist
 
 __all__ = [
     "segment_attention", "segment_lse", "varlen_attention", "varlen_attention_rows", "varlen_lse",
-    "apply_rope_2d", "qk_norm_rope", "rms_norm", "rope_angles", "rope_inv_freq",
+    "uniform_cu_seqlens", "dense_batch_attention",
+    "ROPE_MODES", "apply_rope_2d", "apply_rope_2d_complex", "qk_norm_rope", "rms_norm", "rope_angles", "rope_inv_freq",
     "round_to_bf16", "round_to_f32", "round_to_dtype", "worklist",
 ]

@@ -18,6 +18,14 @@ Readings of the pages taken here (the pages leave these open):
   multiply.  The oracle keeps everything in fp64 and rounds once at storage
   (``rounding.py``); the difference is below one output ulp.
 * ``_qkv_with_rope`` on the vLLM page applies the norm first, then the rotary.
+* ``complex_rope``: ``MultimodalEncoderAttention`` on the tokenspeed page
+  accepts ``position_embedding_mode = "complex_rope"`` and then calls
+  ``packed_qkv_complex_rotary``, whose body is not on the page.  Reading: the
+  complex form of the same rotation -- consecutive elements ``(x[2j], x[2j+1])``
+  are one complex number ``x[2j] + i x[2j+1]``, multiplied by ``e^{i a_j}``
+  with the same ``D/2`` angles ``a_j`` (row table for ``j < D/4``, column
+  table after).  It differs from the rotate-half form only in which elements
+  form a pair: ``(2j, 2j+1)`` instead of ``(j, j + D/2)``.
 """
 from __future__ import annotations
 
@@ -71,6 +79,22 @@ def apply_rope_2d(x: np.ndarray, pos: np.ndarray, theta: float = 10000.0) -> np.
     return x * cos + _rotate_half(x) * sin
 
 
+def apply_rope_2d_complex(x: np.ndarray, pos: np.ndarray, theta: float = 10000.0) -> np.ndarray:
+    """Complex-form RoPE of ``x`` ``[T, H, D]`` (fp64): pair ``j`` is the complex
+    number ``x[..., 2j] + i x[..., 2j+1]``, multiplied by ``exp(i a_j)``."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    ang = rope_angles(pos, D, theta)[:, None, :]     # [T, 1, D/2]
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * ang)
+    y = np.empty_like(x)
+    y[..., 0::2] = z.real
+    y[..., 1::2] = z.imag
+    return y
+
+
+ROPE_MODES = ("neox", "complex")
+
+
 def rms_norm(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
     """``_RMSNorm``: ``x * rsqrt(mean(x**2, -1) + eps) * weight`` (fp64)."""
     x = np.asarray(x, dtype=np.float64)
@@ -80,12 +104,16 @@ def rms_norm(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
 
 def qk_norm_rope(q: np.ndarray, k: np.ndarray, pos: Optional[np.ndarray],
                  theta: float = 10000.0, wq: Optional[np.ndarray] = None,
-                 wk: Optional[np.ndarray] = None, eps: float = 1e-6):
+                 wk: Optional[np.ndarray] = None, eps: float = 1e-6, rope_mode: str = "neox"):
     """The pre-pass on q and k, ``[T, H, D]`` each, in fp64.
 
     Norm (when weights are given) then rotary (when positions are given), the
-    order of ``_qkv_with_rope``.  Returns unrounded fp64 arrays.
+    order of ``_qkv_with_rope``.  ``rope_mode`` is ``"neox"`` (rotate-half) or
+    ``"complex"``.  Returns unrounded fp64 arrays.
     """
+    if rope_mode not in ROPE_MODES:
+        raise ValueError(f"unknown rope mode {rope_mode!r}")
+    rope = apply_rope_2d if rope_mode == "neox" else apply_rope_2d_complex
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     if (wq is None) != (wk is None):
@@ -94,6 +122,6 @@ def qk_norm_rope(q: np.ndarray, k: np.ndarray, pos: Optional[np.ndarray],
         q = rms_norm(q, wq, eps)
         k = rms_norm(k, wk, eps)
     if pos is not None:
-        q = apply_rope_2d(q, pos, theta)
-        k = apply_rope_2d(k, pos, theta)
+        q = rope(q, pos, theta)
+        k = rope(k, pos, theta)
     return q, k

@@ -210,12 +210,12 @@ def test_row_sampler_matches_full_and_blocks_do_not_change_rows(monkeypatch):
 
 # ---- planted mistakes: each pin above must catch a plausible oracle bug -----
 
-def _planted_transposed(q, k, v, scale):
+def _planted_transposed(q, k, v, scale, causal=False):
     # contracts over keys with the wrong operand (k and v swapped)
     return oattn.__dict__["_orig_segment_attention"](q, v, k, scale)
 
 
-def _planted_no_max_subtraction_wrong_axis(q, k, v, scale):
+def _planted_no_max_subtraction_wrong_axis(q, k, v, scale, causal=False):
     q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
     out = np.empty_like(q)
     for h in range(q.shape[1]):
@@ -226,7 +226,7 @@ def _planted_no_max_subtraction_wrong_axis(q, k, v, scale):
     return out
 
 
-def _planted_scale_dropped(q, k, v, scale):
+def _planted_scale_dropped(q, k, v, scale, causal=False):
     return oattn.__dict__["_orig_segment_attention"](q, k, v, 1.0)
 
 

@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=2, help="seeded workload 1..5 (default 2)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--dense-batch", action="store_true",
+                   help="uniform workloads only: attention through vit_dense_batch_attn "
+                        "(cu_seqlens = None form: no work-list, no metadata reads)")
     p.add_argument("--packed-qkv", action="store_true",
                    help="read q, k, v as views of one packed [T, 3, H, D] buffer (token stride 3*H*D)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -217,6 +220,14 @@ def main():
     # The step's first launch: pre-pass and work-list build together.
     fused_args = pre_args[:-1] + wl_args
     f_pre, f_wl, f_at = lib.vit_qk_norm_rope_strided, lib.vit_varlen_worklist, lib.vit_varlen_attn_planned
+    if args.dense_batch:
+        lens = np.diff(x.cu_seqlens)
+        if len(set(lens.tolist())) != 1:
+            sys.exit("bench: --dense-batch needs a workload of equal-length segments")
+        f_at = lib.vit_dense_batch_attn
+        at_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), wl.num_seqs, int(lens[0]), H, D,
+                   float(wl.softmax_scale), dcode, out.data_ptr(), None, strides_arr, sh)
+        at_lse_args = at_args[:-3] + (lse_buf.data_ptr(), strides_arr, sh)
     f_fused = lib.vit_qk_norm_rope_worklist
 
     if args.copy_calibration > 0:
@@ -247,7 +258,10 @@ def main():
     torch.cuda.synchronize()
 
     def step(e=None):
-        check(f_fused(*fused_args))
+        if args.dense_batch:      # no work-list to build
+            check(f_pre(*pre_args))
+        else:
+            check(f_fused(*fused_args))
         if e is not None:
             check(f_hook(e[0].cuda_event, e[1].cuda_event))
         check(f_at(*at_args))
@@ -324,7 +338,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if is_bf16 else "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name + ("_packed_qkv" if args.packed_qkv else ""),
+        "config": {"workload": wl.name + ("_packed_qkv" if args.packed_qkv else "")
+                   + ("_dense_batch" if args.dense_batch else ""),
                    "images": wl.num_seqs, "tokens": T, "heads": H,
                    "head_dim": D, "max_seqlen": wl.max_seqlen, "qk_norm": wl.use_norm,
                    "rope": "2d", "flops_per_step": flops, "parallelism": "none (1 GPU)"},

@@ -184,6 +184,24 @@ int vit_varlen_attn_strided(const void* q, const void* k, const void* v, const i
                             hipStream_t stream);
 
 /*
+ * Attention over a uniform batch: `batch` segments of `seq_len` tokens each,
+ * segment i covering tokens [i * seq_len, (i + 1) * seq_len).  This is the
+ * case _varlen_metadata on the tokenspeed page fills in when cu_seqlens is
+ * None (arange(0, (bsz + 1) * seq_len, seq_len)); the result is that of
+ * vit_varlen_attn_strided on those cu_seqlens, bit for bit.  No cu_seqlens,
+ * work-list or scratch exists: each workgroup derives its segment and q-tile
+ * from its index, so the call allocates nothing and reads no metadata.
+ *  q, k, v, out, lse, strides, dtype, scale   as for vit_varlen_attn_strided
+ *                (T = batch * seq_len rows).
+ *  batch, seq_len   >= 0 (either 0: no-op); batch * seq_len must fit in int32
+ *                and (seq_len + 64) * token stride * 2 must not exceed 2^30
+ *                bytes (VIT_ERR_UNSUPPORTED otherwise).
+ */
+int vit_dense_batch_attn(const void* q, const void* k, const void* v, int batch, int seq_len,
+                         int num_heads, int head_dim, float scale, int dtype, void* out,
+                         float* lse, const int64_t* strides, hipStream_t stream);
+
+/*
  * Query rows per (segment, q-tile) work item of the attention kernel for this
  * shape and dtype, or a negative VIT_ERR_* code for an unsupported shape.
  */

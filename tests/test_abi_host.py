@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
                      "vit_worklist_capacity", "vit_device_error", "vit_last_error", "vit_release",
                      "vit_time_next_kernel", "vit_probe_mfma", "vit_qk_norm_rope_worklist",
                      "vit_varlen_attn_lse", "vit_varlen_attn_strided",
-                     "vit_qk_norm_rope_strided"):
+                     "vit_qk_norm_rope_strided", "vit_dense_batch_attn"):
         assert required in names
     assert sorted(_lib.SIGNATURES) == names
 
@@ -211,3 +211,21 @@ def test_token_stride_errors(lib):
     fused = lib.vit_qk_norm_rope_worklist
     assert fused(FAKE, FAKE + 0x1000, 16, 2, 64, 1, None, 1e4, None, None, 1e-6, _i64(128, 8),
                  FAKE, 3, 10, 64, FAKE, 3, FAKE + 0x40, None) == _lib.VIT_ERR_INVALID_ARG
+
+
+def test_dense_batch_argument_errors(lib):
+    f = lib.vit_dense_batch_attn
+    out = FAKE + 0x1000
+    args = [FAKE, FAKE + 0x100, FAKE + 0x200, 4, 64, 2, 64, 0.125, 1, out, None, None, None]
+    assert f(*args[:3], -1, *args[4:]) == _lib.VIT_ERR_INVALID_ARG
+    assert "batch" in _err(lib)
+    assert f(*args[:4], -2, *args[5:]) == _lib.VIT_ERR_INVALID_ARG
+    assert f(*args[:3], 1 << 20, 1 << 12, *args[5:]) == _lib.VIT_ERR_UNSUPPORTED   # > int32 tokens
+    assert f(*args[:8], 7, *args[9:]) == _lib.VIT_ERR_INVALID_ARG                    # dtype
+    assert f(None, *args[1:]) == _lib.VIT_ERR_INVALID_ARG
+    assert f(*args[:6], 72, *args[7:]) == _lib.VIT_ERR_UNSUPPORTED                   # head dim
+    assert f(*args[:9], FAKE, *args[10:]) == _lib.VIT_ERR_INVALID_ARG                # out aliases q
+    assert f(*args[:3], 2, 1 << 22, *args[5:]) == _lib.VIT_ERR_UNSUPPORTED           # offset span
+    # empty batches are no-ops that touch no memory
+    assert f(*args[:3], 0, 64, *args[5:]) == _lib.VIT_OK
+    assert f(*args[:3], 5, 0, *args[5:]) == _lib.VIT_OK

@@ -36,6 +36,7 @@ SIGNATURES = {
     "vit_varlen_worklist": (_I, [_P, _I, _I, _I, _P, _I64, _P, _P]),
     "vit_varlen_attn_planned": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _I, _F, _I, _P, _P, _P, _P]),
     "vit_varlen_attn_strided": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),
+    "vit_dense_batch_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),
     "vit_varlen_attn_lse": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P]),
     "vit_device_error": (_I, [_P, ctypes.POINTER(ctypes.c_int32), _I]),
     "vit_time_next_kernel": (_I, [_P, _P]),

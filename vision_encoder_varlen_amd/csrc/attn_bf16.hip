@@ -181,8 +181,8 @@ template <class C, bool POS_SCALE>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
-    const int32_t* __restrict__ meta, int H, float scale_log2, u16* __restrict__ out,
-    float* __restrict__ lse, TokenStrides ts) {
+    const int32_t* __restrict__ meta, int u_batch, int u_seq_len, int H, float scale_log2,
+    u16* __restrict__ out, float* __restrict__ lse, TokenStrides ts) {
   constexpr int D = C::D, BN = C::BN, KB = C::KB, STAGES = C::STAGES, NI = C::NI_HI, QB = C::QB;
   // When D is not a multiple of 32 the last 32-row block of O^T has padding
   // rows; row D then collects the row sums of P (see the tile loop), and
@@ -222,7 +222,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     cp_lds[j] = unsigned((is_k ? i * 64 : C::KREG + (i - C::NK) * 64) * 16);
   }
 
-  const int64_t nunits = int64_t(meta[0]) * H;
+  // items == null: a uniform batch (u_batch segments of u_seq_len tokens).
+  const bool uniform = items == nullptr;
+  const int uni_tiles = (u_seq_len + C::BM - 1) / C::BM;
+  const int64_t nunits = (uniform ? int64_t(u_batch) * uni_tiles : int64_t(meta[0])) * H;
   for (int64_t unit = blockIdx.x; unit < nunits; unit += gridDim.x) {
     // The previous unit's output stores (and any copies) are complete, so
     // from here on this wave's vector-memory counter holds only this unit's
@@ -230,10 +233,18 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     const int item = int(unit / H);
     const int h = int(unit - int64_t(item) * H);
-    const int seg = items[2 * item];
-    const int qt = items[2 * item + 1];
-    const int start = cu[seg];
-    const int len = cu[seg + 1] - start;
+    int qt, start, len;
+    if (uniform) {
+      const int seg = item / uni_tiles;
+      qt = item - seg * uni_tiles;
+      start = seg * u_seq_len;
+      len = u_seq_len;
+    } else {
+      const int seg = items[2 * item];
+      qt = items[2 * item + 1];
+      start = cu[seg];
+      len = cu[seg + 1] - start;
+    }
     // Offsets are 32-bit: a segment larger than the addressable span is skipped
     // (the host rejects the max_seqlen that would allow it).  Within the span,
     // every copy offset, padding rows of the last tile included, stays below
@@ -504,18 +515,21 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
 }
 
 template <class C>
-hipError_t launch_cfg(const void* q, const void* k, const void* v, const int32_t* cu,
-                      const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
-                      void* out, float* lse, TokenStrides ts, hipStream_t stream, hipEvent_t e0,
-                      hipEvent_t e1) {
-  const int64_t units = cap * int64_t(H);
+hipError_t launch_cfg(const void* q, const void* k, const void* v, const Schedule& sch, int H,
+                      float scale, void* out, float* lse, TokenStrides ts, hipStream_t stream,
+                      hipEvent_t e0, hipEvent_t e1) {
+  const int64_t items = sch.items != nullptr
+                            ? sch.cap
+                            : int64_t(sch.batch) * ((sch.seq_len + C::BM - 1) / C::BM);
+  const int64_t units = items * int64_t(H);
   if (units <= 0) return hipSuccess;
   const int64_t grid = units < kMaxAttnGrid ? units : kMaxAttnGrid;
   const float c = scale * kLog2e;
   auto kern = c > 0.f ? attn_bf16_kernel<C, true> : attn_bf16_kernel<C, false>;
   hipExtLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), 0, stream, e0, e1, 0,
                      static_cast<const u16*>(q), static_cast<const u16*>(k),
-                     static_cast<const u16*>(v), cu, items, meta, H, c, static_cast<u16*>(out), lse, ts);
+                     static_cast<const u16*>(v), sch.cu, sch.items, sch.meta, sch.batch,
+                     sch.seq_len, H, c, static_cast<u16*>(out), lse, ts);
   return hipGetLastError();
 }
 
@@ -529,27 +543,25 @@ template <> struct Choice<96> { using C = Cfg<96, 4, 1, 32, 4, 2>; };
 template <> struct Choice<128> { using C = Cfg<128, 4, 1, 32, 2, 2>; };
 
 template <int D>
-hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* cu,
-                    const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
-                    void* out, float* lse, TokenStrides ts, hipStream_t stream, hipEvent_t e0,
-                    hipEvent_t e1) {
+hipError_t launch_d(const void* q, const void* k, const void* v, const Schedule& sch, int H,
+                    float scale, void* out, float* lse, TokenStrides ts, hipStream_t stream,
+                    hipEvent_t e0, hipEvent_t e1) {
   using C = typename Choice<D>::C;
   static_assert(C::BM == bf16_block_m_const(D), "work-list block size mismatch");
-  return launch_cfg<C>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
+  return launch_cfg<C>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const int32_t* cu,
-                            const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                            float scale, void* out, float* lse, TokenStrides ts,
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const Schedule& sch,
+                            int H, int D, float scale, void* out, float* lse, TokenStrides ts,
                             hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   switch (D) {
-    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
-    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
-    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
-    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
-    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
+    case 32: return launch_d<32>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
+    case 64: return launch_d<64>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
+    case 80: return launch_d<80>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
+    case 96: return launch_d<96>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
+    case 128: return launch_d<128>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

@@ -29,8 +29,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
-    const int32_t* __restrict__ meta, int H, float scale, float* __restrict__ out,
-    float* __restrict__ lse, TokenStrides ts) {
+    const int32_t* __restrict__ meta, int u_batch, int u_seq_len, int H, float scale,
+    float* __restrict__ out, float* __restrict__ lse, TokenStrides ts) {
   constexpr int HD = D / 2;
   constexpr int ROW = D + 4;  // +16 bytes per LDS row
   __shared__ __align__(16) float ks[kBN * ROW];
@@ -40,14 +40,25 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
   const int r = lane & 31;
   const int half = lane >> 5;
 
-  const int64_t nunits = int64_t(meta[0]) * H;
+  // items == null: a uniform batch (u_batch segments of u_seq_len tokens).
+  const bool uniform = items == nullptr;
+  const int uni_tiles = (u_seq_len + kBM - 1) / kBM;
+  const int64_t nunits = (uniform ? int64_t(u_batch) * uni_tiles : int64_t(meta[0])) * H;
   for (int64_t unit = blockIdx.x; unit < nunits; unit += gridDim.x) {
     const int item = int(unit / H);
     const int h = int(unit - int64_t(item) * H);
-    const int seg = items[2 * item];
-    const int qt = items[2 * item + 1];
-    const int start = cu[seg];
-    const int len = cu[seg + 1] - start;
+    int qt, start, len;
+    if (uniform) {
+      const int seg = item / uni_tiles;
+      qt = item - seg * uni_tiles;
+      start = seg * u_seq_len;
+      len = u_seq_len;
+    } else {
+      const int seg = items[2 * item];
+      qt = items[2 * item + 1];
+      start = cu[seg];
+      len = cu[seg + 1] - start;
+    }
     const int qrow = qt * kBM + r;
 
     float qv[HD], acc[HD];
@@ -113,32 +124,33 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
 }
 
 template <int D>
-hipError_t launch_d(const void* q, const void* k, const void* v, const int32_t* cu,
-                    const int32_t* items, int64_t cap, const int32_t* meta, int H, float scale,
-                    void* out, float* lse, TokenStrides ts, hipStream_t stream, hipEvent_t e0,
-                    hipEvent_t e1) {
-  const int64_t units = cap * int64_t(H);
+hipError_t launch_d(const void* q, const void* k, const void* v, const Schedule& sch, int H,
+                    float scale, void* out, float* lse, TokenStrides ts, hipStream_t stream,
+                    hipEvent_t e0, hipEvent_t e1) {
+  const int64_t items = sch.items != nullptr
+                            ? sch.cap
+                            : int64_t(sch.batch) * ((sch.seq_len + kBM - 1) / kBM);
+  const int64_t units = items * int64_t(H);
   if (units <= 0) return hipSuccess;
   const int64_t grid = units < kMaxAttnGrid ? units : kMaxAttnGrid;
   hipExtLaunchKernelGGL(attn_f32_kernel<D>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, e0, e1, 0,
                      static_cast<const float*>(q), static_cast<const float*>(k),
-                     static_cast<const float*>(v), cu, items, meta, H, scale,
-                     static_cast<float*>(out), lse, ts);
+                     static_cast<const float*>(v), sch.cu, sch.items, sch.meta, sch.batch,
+                     sch.seq_len, H, scale, static_cast<float*>(out), lse, ts);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu,
-                           const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                           float scale, void* out, float* lse, TokenStrides ts,
+hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const Schedule& sch,
+                           int H, int D, float scale, void* out, float* lse, TokenStrides ts,
                            hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   switch (D) {
-    case 32: return launch_d<32>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
-    case 64: return launch_d<64>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
-    case 80: return launch_d<80>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
-    case 96: return launch_d<96>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
-    case 128: return launch_d<128>(q, k, v, cu, items, cap, meta, H, scale, out, lse, ts, stream, e0, e1);
+    case 32: return launch_d<32>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
+    case 64: return launch_d<64>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
+    case 80: return launch_d<80>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
+    case 96: return launch_d<96>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
+    case 128: return launch_d<128>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <map>
 #include <mutex>
@@ -104,23 +105,43 @@ int get_scratch(hipStream_t stream, int64_t cap, Scratch** out) {
   return VIT_OK;
 }
 
-int check_attn_args(const void* q, const void* k, const void* v, const int32_t* cu,
-                    int num_seqs, int max_seqlen, int H, int D, float scale, const void* out) {
-  if (!q || !k || !v || !cu || !out) return fail(VIT_ERR_INVALID_ARG, "null pointer argument");
-  if (num_seqs < 0) return fail(VIT_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
-  if (num_seqs > vit::kWorklistMaxSeqs)
-    return fail(VIT_ERR_UNSUPPORTED, "num_seqs %d exceeds the supported maximum %d", num_seqs,
-                vit::kWorklistMaxSeqs);
-  if (max_seqlen < 0) return fail(VIT_ERR_INVALID_ARG, "max_seqlen must be >= 0 (got %d)", max_seqlen);
+// Checks shared by every attention entry point: the tensors, head count and
+// dim, and the scale.
+int check_tensor_args(const void* q, const void* k, const void* v, int H, int D, float scale,
+                      const void* out) {
+  if (!q || !k || !v || !out) return fail(VIT_ERR_INVALID_ARG, "null pointer argument");
   if (H < 1) return fail(VIT_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", H);
   if (!vit::attn_head_dim_supported(D))
     return fail(VIT_ERR_UNSUPPORTED, "head_dim %d not supported (supported: 32, 64, 80, 96, 128)", D);
   if (!std::isfinite(scale)) return fail(VIT_ERR_INVALID_ARG, "scale must be finite");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(VIT_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
-  if (!aligned4(cu)) return fail(VIT_ERR_INVALID_ARG, "cu_seqlens must be 4-byte aligned");
   if (out == q || out == k || out == v) return fail(VIT_ERR_INVALID_ARG, "out must not alias q, k or v");
   return VIT_OK;
+}
+
+int check_attn_args(const void* q, const void* k, const void* v, const int32_t* cu,
+                    int num_seqs, int max_seqlen, int H, int D, float scale, const void* out) {
+  if (!cu) return fail(VIT_ERR_INVALID_ARG, "null pointer argument");
+  if (num_seqs < 0) return fail(VIT_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (num_seqs > vit::kWorklistMaxSeqs)
+    return fail(VIT_ERR_UNSUPPORTED, "num_seqs %d exceeds the supported maximum %d", num_seqs,
+                vit::kWorklistMaxSeqs);
+  if (max_seqlen < 0) return fail(VIT_ERR_INVALID_ARG, "max_seqlen must be >= 0 (got %d)", max_seqlen);
+  const int rc = check_tensor_args(q, k, v, H, D, scale, out);
+  if (rc != VIT_OK) return rc;
+  if (!aligned4(cu)) return fail(VIT_ERR_INVALID_ARG, "cu_seqlens must be 4-byte aligned");
+  return VIT_OK;
+}
+
+int launch_attn(const void* q, const void* k, const void* v, const vit::Schedule& sch, int H,
+                int D, float scale, int dtype, void* out, float* lse, const vit::TokenStrides& ts,
+                hipStream_t stream, const TimingHook& t) {
+  const hipError_t e =
+      dtype == VIT_BF16
+          ? vit::launch_attn_bf16(q, k, v, sch, H, D, scale, out, lse, ts, stream, t.start, t.stop)
+          : vit::launch_attn_f32(q, k, v, sch, H, D, scale, out, lse, ts, stream, t.start, t.stop);
+  return e == hipSuccess ? ok() : hip_fail(e, "attention launch");
 }
 
 // Token strides (elements) of q, k, v, out from a caller array of n values
@@ -184,13 +205,8 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, 
   hipError_t e = vit::launch_worklist(cu, num_seqs, max_seqlen, bm, items, cap, meta, stream,
                                       nullptr, nullptr);
   if (e != hipSuccess) return hip_fail(e, "work-list launch");
-  e = dtype == VIT_BF16
-          ? vit::launch_attn_bf16(q, k, v, cu, items, cap, meta, H, D, scale, out, lse, ts, stream,
-                                  t.start, t.stop)
-          : vit::launch_attn_f32(q, k, v, cu, items, cap, meta, H, D, scale, out, lse, ts, stream,
-                                 t.start, t.stop);
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
-  return ok();
+  return launch_attn(q, k, v, vit::Schedule{cu, items, meta, cap, 0, 0}, H, D, scale, dtype, out,
+                     lse, ts, stream, t);
 }
 
 int check_prepass_args(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
@@ -376,13 +392,35 @@ int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
     const hipError_t e = record_empty(t, stream);
     return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
   }
-  hipError_t e = dtype == VIT_BF16
-      ? vit::launch_attn_bf16(q, k, v, cu_seqlens, items, cap, meta, num_heads, head_dim, scale,
-                              out, lse, ts, stream, t.start, t.stop)
-      : vit::launch_attn_f32(q, k, v, cu_seqlens, items, cap, meta, num_heads, head_dim, scale,
-                             out, lse, ts, stream, t.start, t.stop);
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
-  return ok();
+  return launch_attn(q, k, v, vit::Schedule{cu_seqlens, items, meta, cap, 0, 0}, num_heads,
+                     head_dim, scale, dtype, out, lse, ts, stream, t);
+}
+
+int vit_dense_batch_attn(const void* q, const void* k, const void* v, int batch, int seq_len,
+                         int num_heads, int head_dim, float scale, int dtype, void* out,
+                         float* lse, const int64_t* strides, hipStream_t stream) {
+  const TimingHook t = take_timing();
+  if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  int rc = check_tensor_args(q, k, v, num_heads, head_dim, scale, out);
+  if (rc != VIT_OK) return rc;
+  if (batch < 0 || seq_len < 0)
+    return fail(VIT_ERR_INVALID_ARG, "batch and seq_len must be >= 0 (got %d, %d)", batch, seq_len);
+  if (int64_t(batch) * seq_len > INT32_MAX)
+    return fail(VIT_ERR_UNSUPPORTED, "batch * seq_len must fit in int32");
+  rc = check_lse(lse, q, k, v, out);
+  if (rc != VIT_OK) return rc;
+  vit::TokenStrides ts{};
+  rc = make_strides(strides, 4, num_heads, head_dim, dtype, &ts);
+  if (rc != VIT_OK) return rc;
+  if (!vit::segment_fits(seq_len, ts.k > ts.v ? ts.k : ts.v))
+    return fail(VIT_ERR_UNSUPPORTED, "(seq_len + %d) * token stride * 2 bytes exceeds %lld",
+                vit::kMaxKeyTile, (long long)vit::kMaxSegmentBytes);
+  if (batch == 0 || seq_len == 0) {
+    const hipError_t e = record_empty(t, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
+  }
+  return launch_attn(q, k, v, vit::Schedule{nullptr, nullptr, nullptr, 0, batch, seq_len},
+                     num_heads, head_dim, scale, dtype, out, lse, ts, stream, t);
 }
 
 int vit_device_error(hipStream_t stream, int32_t* err, int reset) {

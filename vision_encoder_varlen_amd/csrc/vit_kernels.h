@@ -14,6 +14,20 @@ struct TokenStrides {
   int q, k, v, o;
 };
 
+// Where the attention kernels take their (segment, q-tile) items from: a
+// device work-list (items, meta and cu_seqlens), or, with items == null, a
+// uniform batch of `batch` segments of `seq_len` tokens each, segment i
+// starting at token i * seq_len (cu_seqlens = arange(0, (batch+1)*seq_len,
+// seq_len), never stored), taken in index order.
+struct Schedule {
+  const int32_t* cu;
+  const int32_t* items;
+  const int32_t* meta;
+  int64_t cap;  // list capacity (work-list form)
+  int batch;    // uniform form
+  int seq_len;
+};
+
 // Every launch_* takes ev_start / ev_stop: both null, or both timing events
 // that are recorded at its kernel's dispatch start and end (hipExtLaunchKernel).
 
@@ -74,14 +88,12 @@ hipError_t launch_worklist(const int32_t* cu, int N, int max_seqlen, int block_m
                            int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream,
                            hipEvent_t ev_start, hipEvent_t ev_stop);
 
-hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const int32_t* cu,
-                            const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                            float scale, void* out, float* lse, TokenStrides ts,
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const Schedule& sch,
+                            int H, int D, float scale, void* out, float* lse, TokenStrides ts,
                             hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
-hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu,
-                           const int32_t* items, int64_t cap, const int32_t* meta, int H, int D,
-                           float scale, void* out, float* lse, TokenStrides ts,
+hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const Schedule& sch,
+                           int H, int D, float scale, void* out, float* lse, TokenStrides ts,
                            hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 // Attention launches: lse (fp32 [T, H], may be null) receives each row's

@@ -152,6 +152,37 @@ def varlen_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: t
     return out
 
 
+def dense_batch_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, batch: int, seq_len: int,
+                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Attention over a uniform batch of ``batch`` segments of ``seq_len`` tokens
+    (``cu_seqlens = None``), packed ``[batch * seq_len, H, D]``.  No work-list,
+    no metadata, no allocation beyond ``out`` when it is not given."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need_cuda(name, t, q.dtype, token_strided=True)
+        if t.dim() != 3 or t.shape != q.shape:
+            raise ValueError(f"{name} must be [batch * seq_len, H, D] like q")
+    T, H, D = q.shape
+    if T != int(batch) * int(seq_len):
+        raise ValueError(f"q has {T} tokens, expected batch * seq_len = {int(batch) * int(seq_len)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_cuda("out", out, q.dtype, token_strided=True)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if lse is not None:
+        _need_cuda("lse", lse, torch.float32)
+        if lse.shape != (T, H):
+            raise ValueError("lse must be float32 [T, H]")
+    _lib.check(_lib.load().vit_dense_batch_attn(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), int(batch), int(seq_len), H, D, float(scale),
+        dtype_code(q.dtype), out.data_ptr(), _ptr(lse), _strides(q, k, v, out), _stream(q)))
+    return out
+
+
 def attn_block_m(num_heads: int, head_dim: int, dtype: torch.dtype) -> int:
     bm = _lib.load().vit_attn_block_m(num_heads, head_dim, dtype_code(dtype))
     if bm < 0:

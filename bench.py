@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=2, help="seeded workload 1..5 (default 2)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--causal", action="store_true",
+                   help="causal variant (query a sees keys 0..a of its segment); FLOPs count "
+                        "the unmasked pairs, 4*H*D*sum(s*(s+1)/2)")
     p.add_argument("--dense-batch", action="store_true",
                    help="uniform workloads only: attention through vit_dense_batch_attn "
                         "(cu_seqlens = None form: no work-list, no metadata reads)")
@@ -125,7 +128,7 @@ def summarize_pmc(args):
     print(json.dumps(res))
 
 
-def cpu_baseline(wl, x, budget_s):
+def cpu_baseline(wl, x, budget_s, causal=False):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload.
 
     The sample is whole segments (pre-pass + attention), taken in order until the
@@ -145,8 +148,9 @@ def cpu_baseline(wl, x, budget_s):
         i = nseg % wl.num_seqs
         a, b = int(cu[i]), int(cu[i + 1])
         q, k = oracle.qk_norm_rope(x.q[a:b], x.k[a:b], x.pos[a:b], wl.theta, *norm, wl.eps)
-        oracle.segment_attention(q, k, x.v[a:b], wl.softmax_scale)
-        flops += 4.0 * wl.H * wl.D * (b - a) ** 2
+        oracle.segment_attention(q, k, x.v[a:b], wl.softmax_scale, causal)
+        n = b - a
+        flops += 4.0 * wl.H * wl.D * (n * (n + 1) / 2 if causal else n * n)
         nseg += 1
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
@@ -162,7 +166,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path runs on a "
-              "single GPU; see DESIGN.md for how it would shard).", file=sys.stderr)
+              "single GPU).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -210,15 +214,16 @@ def main():
                 float(wl.eps), strides_arr, sh)
     wl_args = (cu.data_ptr(), wl.num_seqs, wl.max_seqlen, bm, plan.items.data_ptr(), plan.cap,
                plan.meta.data_ptr(), sh)
+    flags = 1 if args.causal else 0     # VIT_ATTN_CAUSAL
     at_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), cu.data_ptr(), plan.items.data_ptr(),
-               plan.cap, plan.meta.data_ptr(), H, D, float(wl.softmax_scale), dcode,
+               plan.cap, plan.meta.data_ptr(), H, D, float(wl.softmax_scale), dcode, flags,
                out.data_ptr(), None, strides_arr, sh)
     # The same attention call that also writes the log-sum-exp rows (timed
     # outside the timed loop, for its overhead).
     lse_buf = torch.empty((T, H), dtype=torch.float32, device=dev)
     at_lse_args = at_args[:-3] + (lse_buf.data_ptr(), strides_arr, sh)
     # The step's first launch: pre-pass and work-list build together.
-    fused_args = pre_args[:-1] + wl_args
+    fused_args = pre_args[:11] + (0, strides_arr) + wl_args   # rope_mode 0: rotate-half
     f_pre, f_wl, f_at = lib.vit_qk_norm_rope_strided, lib.vit_varlen_worklist, lib.vit_varlen_attn_planned
     if args.dense_batch:
         lens = np.diff(x.cu_seqlens)
@@ -226,7 +231,7 @@ def main():
             sys.exit("bench: --dense-batch needs a workload of equal-length segments")
         f_at = lib.vit_dense_batch_attn
         at_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), wl.num_seqs, int(lens[0]), H, D,
-                   float(wl.softmax_scale), dcode, out.data_ptr(), None, strides_arr, sh)
+                   float(wl.softmax_scale), dcode, flags, out.data_ptr(), None, strides_arr, sh)
         at_lse_args = at_args[:-3] + (lse_buf.data_ptr(), strides_arr, sh)
     f_fused = lib.vit_qk_norm_rope_worklist
 
@@ -309,6 +314,9 @@ def main():
         sys.exit(3)
 
     flops = wl.attn_flops
+    if args.causal:
+        s_len = np.diff(x.cu_seqlens).astype(np.float64)
+        flops = 4.0 * H * D * float(np.sum(s_len * (s_len + 1) / 2))
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (attn_avg_ms * 1e-3) / 1e12
     is_bf16 = wl.dtype == "bf16"
@@ -339,7 +347,8 @@ def main():
         "dtype": "bf16" if is_bf16 else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name + ("_packed_qkv" if args.packed_qkv else "")
-                   + ("_dense_batch" if args.dense_batch else ""),
+                   + ("_dense_batch" if args.dense_batch else "")
+                   + ("_causal" if args.causal else ""),
                    "images": wl.num_seqs, "tokens": T, "heads": H,
                    "head_dim": D, "max_seqlen": wl.max_seqlen, "qk_norm": wl.use_norm,
                    "rope": "2d", "flops_per_step": flops, "parallelism": "none (1 GPU)"},
@@ -360,7 +369,7 @@ def main():
         result["mfma_ceiling"] = ceiling
         result["roofline"]["frac_of_random_operand_ceiling"] = round(achieved / ceiling["random_bf16"], 4)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, args.causal)
     print(json.dumps(result), flush=True)
 
 

@@ -52,6 +52,20 @@ enum vit_dtype {
   VIT_BF16 = 1  /* bfloat16 (8-bit exponent, 7-bit fraction) */
 };
 
+/* Which elements the 2D rotary embedding pairs (see vit_qk_norm_rope_ex). */
+enum vit_rope_mode {
+  VIT_ROPE_NEOX = 0,   /* rotate-half: pairs (m, m + D/2) */
+  VIT_ROPE_COMPLEX = 1 /* complex form: pairs (2j, 2j + 1) */
+};
+
+/* Attention flags (the `flags` argument of the _ex, planned and dense-batch calls). */
+enum vit_attn_flags {
+  /* Query a of a segment sees keys 0..a of that segment only.  _VisionAttentionBase
+   * on the vLLM page carries is_causal (the encoders pass False); equal query
+   * and key lengths, so the diagonal starts at the segment's first token. */
+  VIT_ATTN_CAUSAL = 1
+};
+
 /* Device-side error bits of one work-list build (vit_varlen_worklist), OR-ed. */
 enum vit_worklist_error {
   VIT_WL_ERR_CU0 = 1,      /* cu_seqlens[0] != 0: the list is empty */
@@ -111,7 +125,25 @@ int vit_qk_norm_rope_strided(void* q, void* k, int64_t total_tokens, int num_hea
                              hipStream_t stream);
 
 /*
- * vit_qk_norm_rope_strided followed by vit_varlen_worklist, in one kernel launch: the
+ * vit_qk_norm_rope_strided with a choice of rotary pairing, rope_mode:
+ *  VIT_ROPE_NEOX     rotate-half, pairs (m, m + D/2) (as vit_qk_norm_rope);
+ *  VIT_ROPE_COMPLEX  the complex form that position_embedding_mode
+ *                    "complex_rope" selects in MultimodalEncoderAttention on
+ *                    the tokenspeed page (packed_qkv_complex_rotary, whose
+ *                    body the page does not show): elements (2j, 2j + 1) form
+ *                    the complex number x[2j] + i x[2j+1], multiplied by
+ *                    exp(i a_j) with the same D/2 angles a_j (row table for
+ *                    j < D/4, column table after).
+ * Any other rope_mode: VIT_ERR_INVALID_ARG.  Other arguments, layout and
+ * errors as for vit_qk_norm_rope_strided.
+ */
+int vit_qk_norm_rope_ex(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
+                        int dtype, const int32_t* pos, float theta, const float* q_weight,
+                        const float* k_weight, float eps, int rope_mode, const int64_t* strides,
+                        hipStream_t stream);
+
+/*
+ * vit_qk_norm_rope_ex followed by vit_varlen_worklist, in one kernel launch: the
  * two are independent, so one extra workgroup of the pre-pass launch builds
  * the work-list while the others normalise and rotate q and k.  Arguments,
  * results and errors are exactly those of the two calls (checked before
@@ -121,9 +153,10 @@ int vit_qk_norm_rope_strided(void* q, void* k, int64_t total_tokens, int num_hea
  */
 int vit_qk_norm_rope_worklist(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
                               int dtype, const int32_t* pos, float theta, const float* q_weight,
-                              const float* k_weight, float eps, const int64_t* strides,
-                              const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int block_m,
-                              int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream);
+                              const float* k_weight, float eps, int rope_mode,
+                              const int64_t* strides, const int32_t* cu_seqlens, int num_seqs,
+                              int max_seqlen, int block_m, int32_t* items, int64_t cap,
+                              int32_t* meta, hipStream_t stream);
 
 /*
  * Varlen attention, bf16 in and out, fp32 accumulation and softmax.
@@ -184,6 +217,17 @@ int vit_varlen_attn_strided(const void* q, const void* k, const void* v, const i
                             hipStream_t stream);
 
 /*
+ * The general form: vit_varlen_attn_strided plus `flags` (enum
+ * vit_attn_flags; 0 = non-causal, exactly vit_varlen_attn_strided).  Unknown
+ * flag bits: VIT_ERR_INVALID_ARG.  With VIT_ATTN_CAUSAL a work item visits
+ * only the key tiles up to its last query row.
+ */
+int vit_varlen_attn_ex(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                       int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
+                       int dtype, int flags, void* out, float* lse, const int64_t* strides,
+                       hipStream_t stream);
+
+/*
  * Attention over a uniform batch: `batch` segments of `seq_len` tokens each,
  * segment i covering tokens [i * seq_len, (i + 1) * seq_len).  This is the
  * case _varlen_metadata on the tokenspeed page fills in when cu_seqlens is
@@ -191,15 +235,15 @@ int vit_varlen_attn_strided(const void* q, const void* k, const void* v, const i
  * vit_varlen_attn_strided on those cu_seqlens, bit for bit.  No cu_seqlens,
  * work-list or scratch exists: each workgroup derives its segment and q-tile
  * from its index, so the call allocates nothing and reads no metadata.
- *  q, k, v, out, lse, strides, dtype, scale   as for vit_varlen_attn_strided
+ *  q, k, v, out, lse, strides, dtype, scale, flags   as for vit_varlen_attn_ex
  *                (T = batch * seq_len rows).
  *  batch, seq_len   >= 0 (either 0: no-op); batch * seq_len must fit in int32
  *                and (seq_len + 64) * token stride * 2 must not exceed 2^30
  *                bytes (VIT_ERR_UNSUPPORTED otherwise).
  */
 int vit_dense_batch_attn(const void* q, const void* k, const void* v, int batch, int seq_len,
-                         int num_heads, int head_dim, float scale, int dtype, void* out,
-                         float* lse, const int64_t* strides, hipStream_t stream);
+                         int num_heads, int head_dim, float scale, int dtype, int flags,
+                         void* out, float* lse, const int64_t* strides, hipStream_t stream);
 
 /*
  * Query rows per (segment, q-tile) work item of the attention kernel for this
@@ -232,7 +276,8 @@ int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
  * cu_seqlens.  Lets one list serve every layer of an encoder tower.
  * dtype selects the bf16 (VIT_BF16) or fp32 (VIT_F32) kernel; lse is as for
  * vit_varlen_attn_lse (null: not written); strides as for
- * vit_varlen_attn_strided (null: contiguous); cap is the capacity the list
+ * vit_varlen_attn_strided (null: contiguous); flags as for vit_varlen_attn_ex;
+ * cap is the capacity the list
  * was built with; the other arguments are those of vit_varlen_attn.  The
  * list's max_seqlen must satisfy the bound vit_varlen_attn checks: the bf16
  * kernel skips a segment beyond the 32-bit offset span (this call cannot see
@@ -241,7 +286,7 @@ int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
 int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
                             const int32_t* cu_seqlens, const int32_t* items, int64_t cap,
                             const int32_t* meta, int num_heads, int head_dim, float scale,
-                            int dtype, void* out, float* lse, const int64_t* strides,
+                            int dtype, int flags, void* out, float* lse, const int64_t* strides,
                             hipStream_t stream);
 
 /*

@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
                      "vit_worklist_capacity", "vit_device_error", "vit_last_error", "vit_release",
                      "vit_time_next_kernel", "vit_probe_mfma", "vit_qk_norm_rope_worklist",
                      "vit_varlen_attn_lse", "vit_varlen_attn_strided",
-                     "vit_qk_norm_rope_strided", "vit_dense_batch_attn"):
+                     "vit_qk_norm_rope_strided", "vit_dense_batch_attn", "vit_qk_norm_rope_ex",
+                     "vit_varlen_attn_ex"):
         assert required in names
     assert sorted(_lib.SIGNATURES) == names
 
@@ -115,15 +116,15 @@ def test_worklist_argument_errors(lib):
 
 def test_planned_argument_errors(lib):
     f = lib.vit_varlen_attn_planned
-    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None, None, None) == 1
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 5, FAKE + 0x100, None, None, None) == 1
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None, None, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, FAKE, 2, 64, 0.1, 1, 0, FAKE + 0x100, None, None, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 5, 0, FAKE + 0x100, None, None, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -4, FAKE, 2, 64, 0.1, 1, 0, FAKE + 0x100, None, None, None) == 1
     # lse must be aligned and must not alias the tensors
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, FAKE + 2, None, None) == 1
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, FAKE + 0x100, None, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, 0, FAKE + 0x100, FAKE + 2, None, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, 0, FAKE + 0x100, FAKE + 0x100, None, None) == 1
     assert "alias" in _err(lib)
     # an empty plan is a no-op
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 2, 64, 0.1, 1, FAKE + 0x100, None, None, None) == 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 2, 64, 0.1, 1, 0, FAKE + 0x100, None, None, None) == 0
 
 
 def test_empty_batch_is_a_no_op(lib):
@@ -163,7 +164,7 @@ def test_probe_argument_errors(lib):
 def test_fused_prepass_worklist_checks_both_argument_sets(lib):
     f = lib.vit_qk_norm_rope_worklist
     meta = FAKE + 0x40
-    ok_pre = (FAKE, FAKE + 0x1000, 16, 2, 64, 1, None, 1e4, None, None, 1e-6, None)
+    ok_pre = (FAKE, FAKE + 0x1000, 16, 2, 64, 1, None, 1e4, None, None, 1e-6, 0, None)
     ok_wl = (FAKE, 3, 10, 64, FAKE, 3, meta, None)
     assert f(None, *ok_pre[1:], *ok_wl) == _lib.VIT_ERR_INVALID_ARG          # pre-pass check
     assert "q or k" in _err(lib)
@@ -206,17 +207,17 @@ def test_token_stride_errors(lib):
     assert p(FAKE, FAKE + 0x100, 0, 2, 64, 1, FAKE, 1e4, None, None, 1e-6, _i64(384, 384),
              None) == _lib.VIT_OK
     planned = lib.vit_varlen_attn_planned
-    assert planned(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, out, None,
+    assert planned(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, 0, out, None,
                    _i64(128, 64, 128, 128), None) == _lib.VIT_ERR_INVALID_ARG
     fused = lib.vit_qk_norm_rope_worklist
-    assert fused(FAKE, FAKE + 0x1000, 16, 2, 64, 1, None, 1e4, None, None, 1e-6, _i64(128, 8),
+    assert fused(FAKE, FAKE + 0x1000, 16, 2, 64, 1, None, 1e4, None, None, 1e-6, 0, _i64(128, 8),
                  FAKE, 3, 10, 64, FAKE, 3, FAKE + 0x40, None) == _lib.VIT_ERR_INVALID_ARG
 
 
 def test_dense_batch_argument_errors(lib):
     f = lib.vit_dense_batch_attn
     out = FAKE + 0x1000
-    args = [FAKE, FAKE + 0x100, FAKE + 0x200, 4, 64, 2, 64, 0.125, 1, out, None, None, None]
+    args = [FAKE, FAKE + 0x100, FAKE + 0x200, 4, 64, 2, 64, 0.125, 1, 0, out, None, None, None]
     assert f(*args[:3], -1, *args[4:]) == _lib.VIT_ERR_INVALID_ARG
     assert "batch" in _err(lib)
     assert f(*args[:4], -2, *args[5:]) == _lib.VIT_ERR_INVALID_ARG
@@ -224,8 +225,39 @@ def test_dense_batch_argument_errors(lib):
     assert f(*args[:8], 7, *args[9:]) == _lib.VIT_ERR_INVALID_ARG                    # dtype
     assert f(None, *args[1:]) == _lib.VIT_ERR_INVALID_ARG
     assert f(*args[:6], 72, *args[7:]) == _lib.VIT_ERR_UNSUPPORTED                   # head dim
-    assert f(*args[:9], FAKE, *args[10:]) == _lib.VIT_ERR_INVALID_ARG                # out aliases q
+    assert f(*args[:10], FAKE, *args[11:]) == _lib.VIT_ERR_INVALID_ARG               # out aliases q
+    assert f(*args[:9], 2, *args[10:]) == _lib.VIT_ERR_INVALID_ARG                   # unknown flag
+    assert "flags" in _err(lib)
     assert f(*args[:3], 2, 1 << 22, *args[5:]) == _lib.VIT_ERR_UNSUPPORTED           # offset span
     # empty batches are no-ops that touch no memory
     assert f(*args[:3], 0, 64, *args[5:]) == _lib.VIT_OK
     assert f(*args[:3], 5, 0, *args[5:]) == _lib.VIT_OK
+
+
+def test_rope_mode_is_checked(lib):
+    f = lib.vit_qk_norm_rope_ex
+    for mode in (-1, 2, 7):
+        assert f(FAKE, FAKE + 0x100, 4, 2, 64, 1, FAKE, 1e4, None, None, 1e-6, mode, None,
+                 None) == _lib.VIT_ERR_INVALID_ARG
+        assert "rope_mode" in _err(lib)
+    # valid modes with no tokens: a no-op
+    for mode in (_lib.VIT_ROPE_NEOX, _lib.VIT_ROPE_COMPLEX):
+        assert f(FAKE, FAKE + 0x100, 0, 2, 64, 1, FAKE, 1e4, None, None, 1e-6, mode, None,
+                 None) == _lib.VIT_OK
+    fused = lib.vit_qk_norm_rope_worklist
+    assert fused(FAKE, FAKE + 0x1000, 16, 2, 64, 1, None, 1e4, None, None, 1e-6, 3, None,
+                 FAKE, 3, 10, 64, FAKE, 3, FAKE + 0x40, None) == _lib.VIT_ERR_INVALID_ARG
+
+
+def test_attention_flags_are_checked(lib):
+    f = lib.vit_varlen_attn_ex
+    base = (FAKE, FAKE + 0x100, FAKE + 0x200, FAKE, 1, 8, 2, 64, 0.125, 1)
+    for flags in (2, 4, -1):
+        assert f(*base, flags, FAKE + 0x1000, None, None, None) == _lib.VIT_ERR_INVALID_ARG
+        assert "flags" in _err(lib)
+    # causal with an empty batch: a no-op
+    assert f(FAKE, FAKE + 0x100, FAKE + 0x200, FAKE, 0, 0, 2, 64, 0.125, 1, _lib.VIT_ATTN_CAUSAL,
+             FAKE + 0x1000, None, None, None) == _lib.VIT_OK
+    planned = lib.vit_varlen_attn_planned
+    assert planned(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, 8, FAKE + 0x100, None,
+                   None, None) == _lib.VIT_ERR_INVALID_ARG

@@ -9,7 +9,7 @@ from gpu_util import assert_prepass_close, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, rope=True, norm=None, theta=10000.0):
+def _run(wl, rope=True, norm=None, theta=10000.0, rope_mode="neox"):
     import torch
     from vision_encoder_varlen_amd import ops
     x = W.generate(wl)
@@ -18,10 +18,11 @@ def _run(wl, rope=True, norm=None, theta=10000.0):
     pos = torch.from_numpy(x.pos).cuda() if rope else None
     wq = torch.from_numpy(x.wq).cuda() if norm else None
     wk = torch.from_numpy(x.wk).cuda() if norm else None
-    ops.qk_norm_rope_(q, k, pos, theta, wq, wk, wl.eps)
+    ops.qk_norm_rope_(q, k, pos, theta, wq, wk, wl.eps, rope_mode=rope_mode)
     torch.cuda.synchronize()
     eq, ek = oracle.qk_norm_rope(x.q, x.k, x.pos if rope else None, theta,
-                                 x.wq if norm else None, x.wk if norm else None, wl.eps)
+                                 x.wq if norm else None, x.wk if norm else None, wl.eps,
+                                 rope_mode=rope_mode)
     return to_host(q), to_host(k), eq, ek, x
 
 
@@ -79,3 +80,39 @@ def test_workload_prepass_sampled_tokens(n):
     it = torch.from_numpy(idx).cuda()
     assert_prepass_close(to_host(q[it]), eq, wl.dtype, f"config {n} q")
     assert_prepass_close(to_host(k[it]), ek, wl.dtype, f"config {n} k")
+
+
+@pytest.mark.parametrize("D", [8, 32, 64, 80, 96, 128, 256])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("norm", [False, True])
+def test_complex_rope_matches_oracle(D, dtype, norm):
+    """Complex-form rotary (pairs (2j, 2j+1)), with and without the norm."""
+    wl = W.custom([(4, 4), (6, 8), (1, 1), (13, 7), (64, 2)], H=3, D=D, dtype=dtype, seed=D + 7)
+    gq, gk, eq, ek, _ = _run(wl, rope=True, norm=norm, rope_mode="complex")
+    assert_prepass_close(gq, eq, dtype, f"complex q D={D}")
+    assert_prepass_close(gk, ek, dtype, f"complex k D={D}")
+
+
+def test_complex_rope_fused_with_worklist_and_strided():
+    """The complex mode through the fused pre-pass + work-list launch on packed
+    [T, 3, H, D] views equals the plain call on contiguous tensors, bit for bit."""
+    import torch
+    from vision_encoder_varlen_amd import ops
+    wl = W.custom([(6, 8), (17, 5), (32, 32)], H=2, D=64, dtype="bf16", seed=12, use_norm=True)
+    x = W.generate(wl)
+    qkv = torch.stack([to_dev(a, "bf16") for a in (x.q, x.k, x.v)], dim=1)
+    q, k = qkv[:, 0], qkv[:, 1]
+    qd, kd = q.contiguous(), k.contiguous()
+    pos = torch.from_numpy(x.pos).cuda()
+    wq, wk = torch.from_numpy(x.wq).cuda(), torch.from_numpy(x.wk).cuda()
+    cu = torch.from_numpy(x.cu_seqlens).cuda()
+    plan = ops.varlen_worklist(cu, wl.max_seqlen, ops.attn_block_m(wl.H, wl.D, q.dtype))
+    ops.qk_norm_rope_(qd, kd, pos, wl.theta, wq, wk, wl.eps, rope_mode="complex")
+    ops.qk_norm_rope_worklist_(q, k, pos, wl.theta, wq, wk, wl.eps, plan, cu, rope_mode="complex")
+    torch.cuda.synchronize()
+    assert torch.equal(q, qd) and torch.equal(k, kd)
+    eq, ek = oracle.qk_norm_rope(x.q, x.k, x.pos, wl.theta, x.wq, x.wk, wl.eps, rope_mode="complex")
+    assert_prepass_close(to_host(q), eq, "bf16", "complex fused q")
+    assert_prepass_close(to_host(k), ek, "bf16", "complex fused k")
+    with pytest.raises(ValueError):
+        ops.qk_norm_rope_(qd, kd, pos, rope_mode="gptj")

@@ -18,6 +18,9 @@ VIT_ERR_UNSUPPORTED = 2
 VIT_ERR_HIP = 3
 VIT_F32 = 0
 VIT_BF16 = 1
+VIT_ROPE_NEOX = 0
+VIT_ROPE_COMPLEX = 1
+VIT_ATTN_CAUSAL = 1
 
 # (name, restype, argtypes) of every function include/vit.h declares.
 _P = ctypes.c_void_p
@@ -27,16 +30,19 @@ _F = ctypes.c_float
 SIGNATURES = {
     "vit_qk_norm_rope": (_I, [_P, _P, _I64, _I, _I, _I, _P, _F, _P, _P, _F, _P]),
     "vit_qk_norm_rope_strided": (_I, [_P, _P, _I64, _I, _I, _I, _P, _F, _P, _P, _F, _P, _P]),
-    "vit_qk_norm_rope_worklist": (_I, [_P, _P, _I64, _I, _I, _I, _P, _F, _P, _P, _F, _P,
+    "vit_qk_norm_rope_ex": (_I, [_P, _P, _I64, _I, _I, _I, _P, _F, _P, _P, _F, _I, _P, _P]),
+    "vit_qk_norm_rope_worklist": (_I, [_P, _P, _I64, _I, _I, _I, _P, _F, _P, _P, _F, _I, _P,
                                        _P, _I, _I, _I, _P, _I64, _P, _P]),
     "vit_varlen_attn": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P]),
     "vit_varlen_attn_f32": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P]),
     "vit_attn_block_m": (_I, [_I, _I, _I]),
     "vit_worklist_capacity": (_I64, [_I, _I, _I]),
     "vit_varlen_worklist": (_I, [_P, _I, _I, _I, _P, _I64, _P, _P]),
-    "vit_varlen_attn_planned": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _I, _F, _I, _P, _P, _P, _P]),
+    "vit_varlen_attn_planned": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _I, _F, _I, _I, _P, _P, _P,
+                                     _P]),
+    "vit_varlen_attn_ex": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
     "vit_varlen_attn_strided": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),
-    "vit_dense_batch_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),
+    "vit_dense_batch_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
     "vit_varlen_attn_lse": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P]),
     "vit_device_error": (_I, [_P, ctypes.POINTER(ctypes.c_int32), _I]),
     "vit_time_next_kernel": (_I, [_P, _P]),

@@ -1,11 +1,14 @@
-// Varlen (block-diagonal) non-causal attention, bf16 in/out, for gfx950.
+// Varlen (block-diagonal) attention, bf16 in/out, for gfx950.
 //
 // Computes, for every work item (segment, q-tile) and head, the rows of
 // softmax(Q K^T * scale) V restricted to the segment (vLLM page
 // vllm.models.dots3_note.nvidia.vision_attention, VisionAttentionV2.forward;
 // tokenspeed page mm_encoder_attention.py, vision_attn_fa3 with
 // cu_seqlens_q = cu_seqlens_k).  The S x S mask of VisionAttention.forward is
-// never formed: each workgroup only visits its own segment's keys.
+// never formed: each workgroup only visits its own segment's keys.  The
+// CAUSAL instantiation (is_causal of _VisionAttentionBase on the vLLM page)
+// also drops keys after each query row, and a work item stops at the key tile
+// holding its last row.
 //
 // Design (one workgroup = WAVES waves; each wave owns 32*QB query rows of
 // one head; two workgroups share a CU so one's softmax overlaps the other's
@@ -177,7 +180,7 @@ __device__ __forceinline__ i16x4_t ds_read_tr16(lds_u16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
 }
 
-template <class C, bool POS_SCALE>
+template <class C, bool POS_SCALE, bool CAUSAL>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
@@ -245,6 +248,15 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       start = cu[seg];
       len = cu[seg + 1] - start;
     }
+    // Causal: a segment's last q-tile visits the most keys, so its tiles are
+    // taken last-first (the heaviest items start first, as in the list order).
+    // An item past the segment's tiles (a list built for other boundaries)
+    // is skipped, as it finds no rows without the reversal.
+    if (CAUSAL) {
+      const int nq = (len + C::BM - 1) / C::BM;
+      if (qt >= nq) continue;
+      qt = nq - 1 - qt;
+    }
     // Offsets are 32-bit: a segment larger than the addressable span is skipped
     // (the host rejects the max_seqlen that would allow it).  Within the span,
     // every copy offset, padding rows of the last tile included, stays below
@@ -287,7 +299,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     for (int b = 0; b < QB; ++b) m_ref[b] = m_seen[b] = -INFINITY;
     f32x16_t o[QB][C::DB];
     float l_run[QB];
-    const int ntiles = (len + BN - 1) / BN;
+    // Keys this unit visits: the whole segment, or with CAUSAL only keys up to
+    // the unit's last query row.
+    const int kv_end = CAUSAL ? min(len, (qt + 1) * C::BM) : len;
+    const int ntiles = (kv_end + BN - 1) / BN;
     auto issue_tile = [&](int t) {
       const unsigned tile_off_k = unsigned(t) * unsigned(BN * 2) * unsigned(ts.k);
       const unsigned tile_off_v = unsigned(t) * unsigned(BN * 2) * unsigned(ts.v);
@@ -312,7 +327,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       }
     };
 
-    // One key tile.  MASKED: the partial last tile.  MODE: kSetRef (tile 0
+    // One key tile.  MASKED: a tile with keys past the segment's end or (with
+    // CAUSAL) after some query row of the unit.  MODE: kSetRef (tile 0
     // of pass 0: its max becomes m_ref), kPlain (exponentials and P V only),
     // kMaxOnly (scores and row max only).
     auto process_tile = [&](auto masked_tag, auto mode_tag, int t) {
@@ -326,8 +342,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       __syncthreads();  // everyone's copies of tile t landed; tile t-1 is free
       if (t + STAGES - 1 < ntiles) issue_tile(t + STAGES - 1);
       if (!wave_active) return;
-
       const int kv0 = t * BN;
+      // Causal: a tile that starts after this wave's last row adds nothing.
+      if (CAUSAL && kv0 > row0 + 32 * QB - 1) return;
+
       const u16* stage = smem + (t % STAGES) * C::STAGE_UNITS * 8;
       // All LDS fragment reads of the tile are issued up front, K first, so
       // their latency is paid once and the V reads land during the scores
@@ -401,6 +419,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
               if constexpr (MASKED) {
                 const int key = kv0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
                 if (key >= len) x = -INFINITY;
+                if (CAUSAL && key > row0 + 32 * b + l32) x = -INFINITY;
               }
               sc[b][kb][r] = x;
             }
@@ -459,14 +478,16 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
 #pragma unroll
       for (int t = 0; t < STAGES - 1; ++t)
         if (t < ntiles) issue_tile(t);
-      const int nfull = len / BN;
+      // Tiles before nfull need no mask: every key is inside the segment and
+      // (causal) at or before the unit's first query row.  The rest are masked.
+      const int nfull = CAUSAL ? min(len, qt * C::BM + 1) / BN : len / BN;
       if (nfull == 0) {
         process_tile(std::true_type{}, m0_tag, 0);
       } else {
         process_tile(std::false_type{}, m0_tag, 0);
         for (int t = 1; t < nfull; ++t) process_tile(std::false_type{}, m_tag, t);
-        if (nfull < ntiles) process_tile(std::true_type{}, m_tag, nfull);
       }
+      for (int t = nfull > 1 ? nfull : 1; t < ntiles; ++t) process_tile(std::true_type{}, m_tag, t);
     };
 
     run_pass(std::integral_constant<int, kSetRef>{}, std::integral_constant<int, kPlain>{});
@@ -516,8 +537,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
 
 template <class C>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, const Schedule& sch, int H,
-                      float scale, void* out, float* lse, TokenStrides ts, hipStream_t stream,
-                      hipEvent_t e0, hipEvent_t e1) {
+                      float scale, bool causal, void* out, float* lse, TokenStrides ts,
+                      hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const int64_t items = sch.items != nullptr
                             ? sch.cap
                             : int64_t(sch.batch) * ((sch.seq_len + C::BM - 1) / C::BM);
@@ -525,7 +546,8 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const Schedul
   if (units <= 0) return hipSuccess;
   const int64_t grid = units < kMaxAttnGrid ? units : kMaxAttnGrid;
   const float c = scale * kLog2e;
-  auto kern = c > 0.f ? attn_bf16_kernel<C, true> : attn_bf16_kernel<C, false>;
+  auto kern = causal ? (c > 0.f ? attn_bf16_kernel<C, true, true> : attn_bf16_kernel<C, false, true>)
+                    : (c > 0.f ? attn_bf16_kernel<C, true, false> : attn_bf16_kernel<C, false, false>);
   hipExtLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), 0, stream, e0, e1, 0,
                      static_cast<const u16*>(q), static_cast<const u16*>(k),
                      static_cast<const u16*>(v), sch.cu, sch.items, sch.meta, sch.batch,
@@ -544,24 +566,24 @@ template <> struct Choice<128> { using C = Cfg<128, 4, 1, 32, 2, 2>; };
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, const Schedule& sch, int H,
-                    float scale, void* out, float* lse, TokenStrides ts, hipStream_t stream,
-                    hipEvent_t e0, hipEvent_t e1) {
+                    float scale, bool causal, void* out, float* lse, TokenStrides ts,
+                    hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   using C = typename Choice<D>::C;
   static_assert(C::BM == bf16_block_m_const(D), "work-list block size mismatch");
-  return launch_cfg<C>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
+  return launch_cfg<C>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const Schedule& sch,
-                            int H, int D, float scale, void* out, float* lse, TokenStrides ts,
-                            hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+                            int H, int D, float scale, bool causal, void* out, float* lse,
+                            TokenStrides ts, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   switch (D) {
-    case 32: return launch_d<32>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
-    case 64: return launch_d<64>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
-    case 80: return launch_d<80>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
-    case 96: return launch_d<96>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
-    case 128: return launch_d<128>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
+    case 32: return launch_d<32>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
+    case 64: return launch_d<64>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
+    case 80: return launch_d<80>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
+    case 96: return launch_d<96>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
+    case 128: return launch_d<128>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,4 +1,4 @@
-// Varlen (block-diagonal) non-causal attention in fp32 throughout.
+// Varlen (block-diagonal) attention in fp32 throughout, non-causal or causal.
 //
 // Same operation as attn_bf16.hip (vLLM page
 // vllm.models.dots3_note.nvidia.vision_attention, VisionAttentionV2.forward),
@@ -25,7 +25,7 @@ constexpr int kBM = kBlockMF32;
 constexpr int kBN = 32;
 constexpr int kThreads = 64;
 
-template <int D>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
@@ -76,14 +76,16 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
       for (int d = 0; d < HD; ++d) qv[d] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
+    // Keys visited: the segment, or with CAUSAL those up to the unit's last row.
+    const int kv_end = CAUSAL ? min(len, qt * kBM + kBM) : len;
 
-    for (int kv0 = 0; kv0 < len; kv0 += kBN) {
+    for (int kv0 = 0; kv0 < kv_end; kv0 += kBN) {
       __syncthreads();  // previous tile fully consumed
       for (int c = lane; c < kBN * (D / 4); c += kThreads) {
         const int key = c / (D / 4);
         const int dc = c - key * (D / 4);
         float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
-        if (kv0 + key < len) {
+        if (kv0 + key < kv_end) {
           const size_t tok = size_t(start + kv0 + key);
           kx = *reinterpret_cast<const float4*>(k + tok * ts.k + size_t(h) * D + dc * 4);
           vx = *reinterpret_cast<const float4*>(v + tok * ts.v + size_t(h) * D + dc * 4);
@@ -92,13 +94,16 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
         *reinterpret_cast<float4*>(vs + key * ROW + dc * 4) = vx;
       }
       __syncthreads();
-      const int nk = len - kv0 < kBN ? len - kv0 : kBN;
+      const int nk = kv_end - kv0 < kBN ? kv_end - kv0 : kBN;
       for (int j = 0; j < nk; ++j) {
         const float* kr = ks + j * ROW + half * HD;
         float part = 0.f;
 #pragma unroll
         for (int d = 0; d < HD; ++d) part = fmaf(qv[d], kr[d], part);
-        const float sc = (part + __shfl_xor(part, 32)) * scale;
+        const float dot = part + __shfl_xor(part, 32);
+        // Causal: keys after this row get weight zero (key 0 always comes
+        // first, so m is finite before any such key).
+        const float sc = CAUSAL && kv0 + j > qrow ? -INFINITY : dot * scale;
         const float m_new = fmaxf(m, sc);
         const float alpha = expf(m - m_new);
         const float p = expf(sc - m_new);
@@ -125,15 +130,16 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, const Schedule& sch, int H,
-                    float scale, void* out, float* lse, TokenStrides ts, hipStream_t stream,
-                    hipEvent_t e0, hipEvent_t e1) {
+                    float scale, bool causal, void* out, float* lse, TokenStrides ts,
+                    hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const int64_t items = sch.items != nullptr
                             ? sch.cap
                             : int64_t(sch.batch) * ((sch.seq_len + kBM - 1) / kBM);
   const int64_t units = items * int64_t(H);
   if (units <= 0) return hipSuccess;
   const int64_t grid = units < kMaxAttnGrid ? units : kMaxAttnGrid;
-  hipExtLaunchKernelGGL(attn_f32_kernel<D>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, e0, e1, 0,
+  auto kern = causal ? attn_f32_kernel<D, true> : attn_f32_kernel<D, false>;
+  hipExtLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), 0, stream, e0, e1, 0,
                      static_cast<const float*>(q), static_cast<const float*>(k),
                      static_cast<const float*>(v), sch.cu, sch.items, sch.meta, sch.batch,
                      sch.seq_len, H, scale, static_cast<float*>(out), lse, ts);
@@ -143,14 +149,14 @@ hipError_t launch_d(const void* q, const void* k, const void* v, const Schedule&
 }  // namespace
 
 hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const Schedule& sch,
-                           int H, int D, float scale, void* out, float* lse, TokenStrides ts,
-                           hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+                           int H, int D, float scale, bool causal, void* out, float* lse,
+                           TokenStrides ts, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   switch (D) {
-    case 32: return launch_d<32>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
-    case 64: return launch_d<64>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
-    case 80: return launch_d<80>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
-    case 96: return launch_d<96>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
-    case 128: return launch_d<128>(q, k, v, sch, H, scale, out, lse, ts, stream, e0, e1);
+    case 32: return launch_d<32>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
+    case 64: return launch_d<64>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
+    case 80: return launch_d<80>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
+    case 96: return launch_d<96>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
+    case 128: return launch_d<128>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

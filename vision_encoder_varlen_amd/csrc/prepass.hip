@@ -7,7 +7,9 @@
 // next D/4, applied rotate-half to pairs (m, m + D/2) -- the native rotary
 // branch of MultimodalEncoderAttention.forward on the tokenspeed page
 // mm_encoder_attention.py widens a half-width cosine the same way.  Order: norm,
-// then rotary (_qkv_with_rope).
+// then rotary (_qkv_with_rope).  The complex form (position_embedding_mode
+// "complex_rope" on the tokenspeed page) turns the same angles on the pairs
+// (2j, 2j + 1) instead.
 //
 // Memory-bound.  A workgroup takes a group of tokens:
 //  1. cos/sin of the token group's D/2 angles go to LDS, so each angle is
@@ -105,7 +107,7 @@ template <typename T, int E>
 __global__ __launch_bounds__(kThreads) void prepass_kernel(
     T* __restrict__ q, T* __restrict__ k, long long T_tok, int H, int D, int G, int tok_per_grp,
     const int32_t* __restrict__ pos, Freqs freqs, const float* __restrict__ wq,
-    const float* __restrict__ wk, float eps, WorklistJob job, int qs, int ks) {
+    const float* __restrict__ wk, float eps, WorklistJob job, int qs, int ks, int rope_mode) {
   extern __shared__ float2 cs[];  // [tok_per_grp][D/2] (cos, sin)
   __shared__ int s_wave[kThreads / 64];
   // With a work-list job workgroup 0 (dispatched first) builds the list,
@@ -206,7 +208,9 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
           }
         }
       }
-      if (rope && row_ok) {
+      if (rope && row_ok && rope_mode == 0) {
+        // Rotate-half: element m of the first half pairs with m + D/2 and
+        // turns by angle m.
         const float2* c = cs + tl * half_d + m0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -217,6 +221,25 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
             const float yb = b[which][e] * cse.x + a[which][e] * cse.y;
             a[which][e] = ya;
             b[which][e] = yb;
+          }
+        }
+      } else if (rope && row_ok) {
+        // Complex form: elements (2j, 2j+1) are one complex number turned by
+        // angle j.  This lane's first-half dims hold pairs m0/2 .., its
+        // second-half dims pairs D/4 + m0/2 ..
+        const float2* ca = cs + tl * half_d + m0 / 2;
+        const float2* cb = ca + quarter_d;
+#pragma unroll
+        for (int i = 0; i < E / 2; ++i) {
+          const float2 c1 = ca[i], c2 = cb[i];
+#pragma unroll
+          for (int which = 0; which < 2; ++which) {
+            const float a0 = a[which][2 * i], a1 = a[which][2 * i + 1];
+            a[which][2 * i] = a0 * c1.x - a1 * c1.y;
+            a[which][2 * i + 1] = a1 * c1.x + a0 * c1.y;
+            const float b0 = b[which][2 * i], b1 = b[which][2 * i + 1];
+            b[which][2 * i] = b0 * c2.x - b1 * c2.y;
+            b[which][2 * i + 1] = b1 * c2.x + b0 * c2.y;
           }
         }
       }
@@ -236,7 +259,8 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
 hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
                           const int32_t* pos, const double* inv_freq_host, const float* wq,
                           const float* wk, float eps, hipStream_t stream, hipEvent_t e0,
-                          hipEvent_t e1, const WorklistJob* job, int q_stride, int k_stride) {
+                          hipEvent_t e1, const WorklistJob* job, int q_stride, int k_stride,
+                          int rope_mode) {
   const int qs = q_stride > 0 ? q_stride : H * D;
   const int ks = k_stride > 0 ? k_stride : H * D;
   WorklistJob jb{};
@@ -287,15 +311,15 @@ hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
   if (dtype == 1 && E == 8) {
     hipExtLaunchKernelGGL(prepass_kernel<u16, 8>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
                           e0, e1, 0, static_cast<u16*>(q), static_cast<u16*>(k), (long long)T, H, D,
-                          G, tok_per_grp, pos, fr, wq, wk, eps, jb, qs, ks);
+                          G, tok_per_grp, pos, fr, wq, wk, eps, jb, qs, ks, rope_mode);
   } else if (dtype == 1) {
     hipExtLaunchKernelGGL(prepass_kernel<u16, 4>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
                           e0, e1, 0, static_cast<u16*>(q), static_cast<u16*>(k), (long long)T, H, D,
-                          G, tok_per_grp, pos, fr, wq, wk, eps, jb, qs, ks);
+                          G, tok_per_grp, pos, fr, wq, wk, eps, jb, qs, ks, rope_mode);
   } else {
     hipExtLaunchKernelGGL(prepass_kernel<float, 4>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
                           e0, e1, 0, static_cast<float*>(q), static_cast<float*>(k), (long long)T, H,
-                          D, G, tok_per_grp, pos, fr, wq, wk, eps, jb, qs, ks);
+                          D, G, tok_per_grp, pos, fr, wq, wk, eps, jb, qs, ks, rope_mode);
   }
   return hipGetLastError();
 }

@@ -134,13 +134,21 @@ int check_attn_args(const void* q, const void* k, const void* v, const int32_t* 
   return VIT_OK;
 }
 
+int check_flags(int flags) {
+  if (flags & ~VIT_ATTN_CAUSAL) return fail(VIT_ERR_INVALID_ARG, "unknown attention flags 0x%x", flags);
+  return VIT_OK;
+}
+
 int launch_attn(const void* q, const void* k, const void* v, const vit::Schedule& sch, int H,
-                int D, float scale, int dtype, void* out, float* lse, const vit::TokenStrides& ts,
-                hipStream_t stream, const TimingHook& t) {
+                int D, float scale, int dtype, int flags, void* out, float* lse,
+                const vit::TokenStrides& ts, hipStream_t stream, const TimingHook& t) {
+  const bool causal = (flags & VIT_ATTN_CAUSAL) != 0;
   const hipError_t e =
       dtype == VIT_BF16
-          ? vit::launch_attn_bf16(q, k, v, sch, H, D, scale, out, lse, ts, stream, t.start, t.stop)
-          : vit::launch_attn_f32(q, k, v, sch, H, D, scale, out, lse, ts, stream, t.start, t.stop);
+          ? vit::launch_attn_bf16(q, k, v, sch, H, D, scale, causal, out, lse, ts, stream, t.start,
+                                  t.stop)
+          : vit::launch_attn_f32(q, k, v, sch, H, D, scale, causal, out, lse, ts, stream, t.start,
+                                 t.stop);
   return e == hipSuccess ? ok() : hip_fail(e, "attention launch");
 }
 
@@ -177,10 +185,12 @@ int block_m_for(int dtype, int D) {
 }
 
 int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, int num_seqs,
-                int max_seqlen, int H, int D, float scale, void* out, float* lse,
+                int max_seqlen, int H, int D, float scale, int flags, void* out, float* lse,
                 const int64_t* strides, hipStream_t stream, int dtype) {
   const TimingHook t = take_timing();
   int rc = check_attn_args(q, k, v, cu, num_seqs, max_seqlen, H, D, scale, out);
+  if (rc != VIT_OK) return rc;
+  rc = check_flags(flags);
   if (rc != VIT_OK) return rc;
   rc = check_lse(lse, q, k, v, out);
   if (rc != VIT_OK) return rc;
@@ -205,14 +215,16 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, 
   hipError_t e = vit::launch_worklist(cu, num_seqs, max_seqlen, bm, items, cap, meta, stream,
                                       nullptr, nullptr);
   if (e != hipSuccess) return hip_fail(e, "work-list launch");
-  return launch_attn(q, k, v, vit::Schedule{cu, items, meta, cap, 0, 0}, H, D, scale, dtype, out,
-                     lse, ts, stream, t);
+  return launch_attn(q, k, v, vit::Schedule{cu, items, meta, cap, 0, 0}, H, D, scale, dtype, flags,
+                     out, lse, ts, stream, t);
 }
 
 int check_prepass_args(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
                        int dtype, const int32_t* pos, float theta, const float* q_weight,
-                       const float* k_weight, float eps) {
+                       const float* k_weight, float eps, int rope_mode) {
   if (!q || !k) return fail(VIT_ERR_INVALID_ARG, "null q or k");
+  if (rope_mode != VIT_ROPE_NEOX && rope_mode != VIT_ROPE_COMPLEX)
+    return fail(VIT_ERR_INVALID_ARG, "unknown rope_mode %d", rope_mode);
   if (total_tokens < 0) return fail(VIT_ERR_INVALID_ARG, "total_tokens must be >= 0");
   if (num_heads < 1) return fail(VIT_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", num_heads);
   if (head_dim < 8 || head_dim > 256 || head_dim % 8 != 0)
@@ -254,8 +266,9 @@ int check_worklist_args(const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
 // or null.
 int launch_prepass_job(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
                        int dtype, const int32_t* pos, float theta, const float* q_weight,
-                       const float* k_weight, float eps, const vit::WorklistJob* job,
-                       const vit::TokenStrides& ts, hipStream_t stream, const TimingHook& t) {
+                       const float* k_weight, float eps, int rope_mode,
+                       const vit::WorklistJob* job, const vit::TokenStrides& ts,
+                       hipStream_t stream, const TimingHook& t) {
   const bool prepass_work = total_tokens > 0 && (pos != nullptr || q_weight != nullptr);
   if (!prepass_work && job == nullptr) {
     const hipError_t e = record_empty(t, stream);
@@ -267,7 +280,7 @@ int launch_prepass_job(void* q, void* k, int64_t total_tokens, int num_heads, in
   for (int j = 0; j < F; ++j) inv_freq[j] = std::pow(double(theta), -2.0 * j / (head_dim / 2.0));
   hipError_t e = vit::launch_prepass(q, k, total_tokens, num_heads, head_dim, dtype, pos, inv_freq,
                                      q_weight, k_weight, eps, stream, t.start, t.stop, job, ts.q,
-                                     ts.k);
+                                     ts.k, rope_mode);
   if (e != hipSuccess) return hip_fail(e, job ? "pre-pass + work-list launch" : "pre-pass launch");
   return ok();
 }
@@ -287,25 +300,34 @@ int vit_qk_norm_rope_strided(void* q, void* k, int64_t total_tokens, int num_hea
                              int dtype, const int32_t* pos, float theta, const float* q_weight,
                              const float* k_weight, float eps, const int64_t* strides,
                              hipStream_t stream) {
+  return vit_qk_norm_rope_ex(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta, q_weight,
+                             k_weight, eps, VIT_ROPE_NEOX, strides, stream);
+}
+
+int vit_qk_norm_rope_ex(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
+                        int dtype, const int32_t* pos, float theta, const float* q_weight,
+                        const float* k_weight, float eps, int rope_mode, const int64_t* strides,
+                        hipStream_t stream) {
   const TimingHook t = take_timing();
   int rc = check_prepass_args(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta,
-                              q_weight, k_weight, eps);
+                              q_weight, k_weight, eps, rope_mode);
   if (rc != VIT_OK) return rc;
   vit::TokenStrides ts{};
   rc = make_strides(strides, 2, num_heads, head_dim, dtype, &ts);
   if (rc != VIT_OK) return rc;
   return launch_prepass_job(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta, q_weight,
-                            k_weight, eps, nullptr, ts, stream, t);
+                            k_weight, eps, rope_mode, nullptr, ts, stream, t);
 }
 
 int vit_qk_norm_rope_worklist(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
                               int dtype, const int32_t* pos, float theta, const float* q_weight,
-                              const float* k_weight, float eps, const int64_t* strides,
-                              const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int block_m,
-                              int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream) {
+                              const float* k_weight, float eps, int rope_mode,
+                              const int64_t* strides, const int32_t* cu_seqlens, int num_seqs,
+                              int max_seqlen, int block_m, int32_t* items, int64_t cap,
+                              int32_t* meta, hipStream_t stream) {
   const TimingHook t = take_timing();
   int rc = check_prepass_args(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta, q_weight,
-                              k_weight, eps);
+                              k_weight, eps, rope_mode);
   if (rc != VIT_OK) return rc;
   vit::TokenStrides ts{};
   rc = make_strides(strides, 2, num_heads, head_dim, dtype, &ts);
@@ -314,20 +336,20 @@ int vit_qk_norm_rope_worklist(void* q, void* k, int64_t total_tokens, int num_he
   if (rc != VIT_OK) return rc;
   const vit::WorklistJob job{cu_seqlens, num_seqs, 0, max_seqlen, block_m, items, cap, meta};
   return launch_prepass_job(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta, q_weight,
-                            k_weight, eps, &job, ts, stream, t);
+                            k_weight, eps, rope_mode, &job, ts, stream, t);
 }
 
 int vit_varlen_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                     int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
                     void* out, hipStream_t stream) {
-  return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, out,
+  return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, 0, out,
                      nullptr, nullptr, stream, VIT_BF16);
 }
 
 int vit_varlen_attn_f32(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                         int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
                         void* out, hipStream_t stream) {
-  return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, out,
+  return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, 0, out,
                      nullptr, nullptr, stream, VIT_F32);
 }
 
@@ -335,7 +357,7 @@ int vit_varlen_attn_lse(const void* q, const void* k, const void* v, const int32
                         int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
                         int dtype, void* out, float* lse, hipStream_t stream) {
   if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-  return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, out,
+  return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, 0, out,
                      lse, nullptr, stream, dtype);
 }
 
@@ -343,9 +365,17 @@ int vit_varlen_attn_strided(const void* q, const void* k, const void* v, const i
                             int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
                             int dtype, void* out, float* lse, const int64_t* strides,
                             hipStream_t stream) {
+  return vit_varlen_attn_ex(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale,
+                            dtype, 0, out, lse, strides, stream);
+}
+
+int vit_varlen_attn_ex(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                       int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
+                       int dtype, int flags, void* out, float* lse, const int64_t* strides,
+                       hipStream_t stream) {
   if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-  return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, out,
-                     lse, strides, stream, dtype);
+  return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, flags,
+                     out, lse, strides, stream, dtype);
 }
 
 int vit_attn_block_m(int num_heads, int head_dim, int dtype) {
@@ -375,12 +405,14 @@ int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
 int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
                             const int32_t* cu_seqlens, const int32_t* items, int64_t cap,
                             const int32_t* meta, int num_heads, int head_dim, float scale,
-                            int dtype, void* out, float* lse, const int64_t* strides,
+                            int dtype, int flags, void* out, float* lse, const int64_t* strides,
                             hipStream_t stream) {
   const TimingHook t = take_timing();
   if (!items || !meta) return fail(VIT_ERR_INVALID_ARG, "null work-list pointer");
   if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   int rc = check_attn_args(q, k, v, cu_seqlens, 0, 0, num_heads, head_dim, scale, out);
+  if (rc != VIT_OK) return rc;
+  rc = check_flags(flags);
   if (rc != VIT_OK) return rc;
   if (cap < 0 || cap > kMaxCapacity) return fail(VIT_ERR_INVALID_ARG, "bad work-list capacity %lld", (long long)cap);
   rc = check_lse(lse, q, k, v, out);
@@ -393,15 +425,17 @@ int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
     return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
   }
   return launch_attn(q, k, v, vit::Schedule{cu_seqlens, items, meta, cap, 0, 0}, num_heads,
-                     head_dim, scale, dtype, out, lse, ts, stream, t);
+                     head_dim, scale, dtype, flags, out, lse, ts, stream, t);
 }
 
 int vit_dense_batch_attn(const void* q, const void* k, const void* v, int batch, int seq_len,
-                         int num_heads, int head_dim, float scale, int dtype, void* out,
-                         float* lse, const int64_t* strides, hipStream_t stream) {
+                         int num_heads, int head_dim, float scale, int dtype, int flags,
+                         void* out, float* lse, const int64_t* strides, hipStream_t stream) {
   const TimingHook t = take_timing();
   if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   int rc = check_tensor_args(q, k, v, num_heads, head_dim, scale, out);
+  if (rc != VIT_OK) return rc;
+  rc = check_flags(flags);
   if (rc != VIT_OK) return rc;
   if (batch < 0 || seq_len < 0)
     return fail(VIT_ERR_INVALID_ARG, "batch and seq_len must be >= 0 (got %d, %d)", batch, seq_len);
@@ -420,7 +454,7 @@ int vit_dense_batch_attn(const void* q, const void* k, const void* v, int batch,
     return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
   }
   return launch_attn(q, k, v, vit::Schedule{nullptr, nullptr, nullptr, 0, batch, seq_len},
-                     num_heads, head_dim, scale, dtype, out, lse, ts, stream, t);
+                     num_heads, head_dim, scale, dtype, flags, out, lse, ts, stream, t);
 }
 
 int vit_device_error(hipStream_t stream, int32_t* err, int reset) {

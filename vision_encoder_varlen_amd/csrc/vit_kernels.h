@@ -82,19 +82,23 @@ hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
                           const int32_t* pos, const double* inv_freq_host,
                           const float* wq, const float* wk, float eps, hipStream_t stream,
                           hipEvent_t ev_start, hipEvent_t ev_stop,
-                          const WorklistJob* job = nullptr, int q_stride = 0, int k_stride = 0);
+                          const WorklistJob* job = nullptr, int q_stride = 0, int k_stride = 0,
+                          int rope_mode = 0);
 
 hipError_t launch_worklist(const int32_t* cu, int N, int max_seqlen, int block_m,
                            int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream,
                            hipEvent_t ev_start, hipEvent_t ev_stop);
 
+// causal: query row a of a segment sees keys 0..a of that segment only.
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const Schedule& sch,
-                            int H, int D, float scale, void* out, float* lse, TokenStrides ts,
-                            hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+                            int H, int D, float scale, bool causal, void* out, float* lse,
+                            TokenStrides ts, hipStream_t stream, hipEvent_t ev_start,
+                            hipEvent_t ev_stop);
 
 hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const Schedule& sch,
-                           int H, int D, float scale, void* out, float* lse, TokenStrides ts,
-                           hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+                           int H, int D, float scale, bool causal, void* out, float* lse,
+                           TokenStrides ts, hipStream_t stream, hipEvent_t ev_start,
+                           hipEvent_t ev_stop);
 
 // Attention launches: lse (fp32 [T, H], may be null) receives each row's
 // log-sum-exp of scores, natural log.

@@ -71,21 +71,34 @@ def _prepass_checks(q, k, pos, q_weight, k_weight) -> None:
                 raise ValueError(f"{name} must be float32 [D]")
 
 
+_ROPE_MODES = {"neox": _lib.VIT_ROPE_NEOX, "complex": _lib.VIT_ROPE_COMPLEX}
+
+
+def _rope_mode(mode: str) -> int:
+    if mode not in _ROPE_MODES:
+        raise ValueError(f"unknown rope mode {mode!r}; expected 'neox' or 'complex'")
+    return _ROPE_MODES[mode]
+
+
 def qk_norm_rope_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch.Tensor] = None,
                   theta: float = 10000.0, q_weight: Optional[torch.Tensor] = None,
-                  k_weight: Optional[torch.Tensor] = None, eps: float = 1e-6) -> None:
-    """In-place Q/K RMSNorm (when weights are given) then 2D rotary (when ``pos`` is given)."""
+                  k_weight: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                  rope_mode: str = "neox") -> None:
+    """In-place Q/K RMSNorm (when weights are given) then 2D rotary (when ``pos`` is given).
+
+    ``rope_mode``: ``"neox"`` pairs ``(m, m + D/2)``; ``"complex"`` pairs ``(2j, 2j + 1)``."""
     _prepass_checks(q, k, pos, q_weight, k_weight)
     T, H, D = q.shape
-    _lib.check(_lib.load().vit_qk_norm_rope_strided(
+    _lib.check(_lib.load().vit_qk_norm_rope_ex(
         q.data_ptr(), k.data_ptr(), T, H, D, dtype_code(q.dtype), _ptr(pos), float(theta),
-        _ptr(q_weight), _ptr(k_weight), float(eps), _strides(q, k), _stream(q)))
+        _ptr(q_weight), _ptr(k_weight), float(eps), _rope_mode(rope_mode), _strides(q, k),
+        _stream(q)))
 
 
 def qk_norm_rope_worklist_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch.Tensor],
                            theta: float, q_weight: Optional[torch.Tensor],
                            k_weight: Optional[torch.Tensor], eps: float, plan: "Plan",
-                           cu_seqlens: torch.Tensor) -> "Plan":
+                           cu_seqlens: torch.Tensor, rope_mode: str = "neox") -> "Plan":
     """``qk_norm_rope_`` and ``rebuild_worklist(plan, cu_seqlens)`` in one launch."""
     _prepass_checks(q, k, pos, q_weight, k_weight)
     _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
@@ -94,7 +107,8 @@ def qk_norm_rope_worklist_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch
     T, H, D = q.shape
     _lib.check(_lib.load().vit_qk_norm_rope_worklist(
         q.data_ptr(), k.data_ptr(), T, H, D, dtype_code(q.dtype), _ptr(pos), float(theta),
-        _ptr(q_weight), _ptr(k_weight), float(eps), _strides(q, k), cu_seqlens.data_ptr(), plan.num_seqs,
+        _ptr(q_weight), _ptr(k_weight), float(eps), _rope_mode(rope_mode), _strides(q, k),
+        cu_seqlens.data_ptr(), plan.num_seqs,
         plan.max_seqlen, plan.block_m, plan.items.data_ptr(), plan.cap, plan.meta.data_ptr(),
         _stream(q)))
     return plan
@@ -115,8 +129,10 @@ def _attn_checks(q, k, v, cu_seqlens):
 
 def varlen_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                 max_seqlen: int, scale: Optional[float] = None,
-                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Block-diagonal non-causal attention over packed ``[T, H, D]`` tensors.
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                causal: bool = False) -> torch.Tensor:
+    """Block-diagonal attention over packed ``[T, H, D]`` tensors (non-causal
+    unless ``causal``: then query ``a`` of a segment sees keys ``0..a`` of it).
 
     ``scale`` defaults to ``head_dim ** -0.5``.  Dispatches on dtype: bf16 uses
     the MFMA kernel, fp32 the fp32 kernel.  ``lse`` (optional, fp32 ``[T, H]``)
@@ -138,11 +154,11 @@ def varlen_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: t
             raise ValueError("lse must be float32 [T, H]")
     lib = _lib.load()
     strides = _strides(q, k, v, out)
-    if lse is not None or strides is not None:
-        _lib.check(lib.vit_varlen_attn_strided(
+    if lse is not None or strides is not None or causal:
+        _lib.check(lib.vit_varlen_attn_ex(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
-            int(max_seqlen), H, D, float(scale), dtype_code(q.dtype), out.data_ptr(), _ptr(lse),
-            strides, _stream(q)))
+            int(max_seqlen), H, D, float(scale), dtype_code(q.dtype), _flags(causal),
+            out.data_ptr(), _ptr(lse), strides, _stream(q)))
         return out
     fn = lib.vit_varlen_attn if q.dtype == torch.bfloat16 else lib.vit_varlen_attn_f32
     dtype_code(q.dtype)
@@ -152,9 +168,13 @@ def varlen_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: t
     return out
 
 
+def _flags(causal: bool) -> int:
+    return _lib.VIT_ATTN_CAUSAL if causal else 0
+
+
 def dense_batch_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, batch: int, seq_len: int,
                      scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                     lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     lse: Optional[torch.Tensor] = None, causal: bool = False) -> torch.Tensor:
     """Attention over a uniform batch of ``batch`` segments of ``seq_len`` tokens
     (``cu_seqlens = None``), packed ``[batch * seq_len, H, D]``.  No work-list,
     no metadata, no allocation beyond ``out`` when it is not given."""
@@ -179,7 +199,8 @@ def dense_batch_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, batch: i
             raise ValueError("lse must be float32 [T, H]")
     _lib.check(_lib.load().vit_dense_batch_attn(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), int(batch), int(seq_len), H, D, float(scale),
-        dtype_code(q.dtype), out.data_ptr(), _ptr(lse), _strides(q, k, v, out), _stream(q)))
+        dtype_code(q.dtype), _flags(causal), out.data_ptr(), _ptr(lse), _strides(q, k, v, out),
+        _stream(q)))
     return out
 
 
@@ -235,7 +256,7 @@ def rebuild_worklist(plan: Plan, cu_seqlens: torch.Tensor) -> Plan:
 def varlen_attn_planned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                         cu_seqlens: torch.Tensor, plan: Plan, scale: Optional[float] = None,
                         out: Optional[torch.Tensor] = None,
-                        lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+                        lse: Optional[torch.Tensor] = None, causal: bool = False) -> torch.Tensor:
     """Attention over a work-list from ``varlen_worklist`` (built with ``attn_block_m``)."""
     _attn_checks(q, k, v, cu_seqlens)
     T, H, D = q.shape
@@ -255,8 +276,8 @@ def varlen_attn_planned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             raise ValueError("lse must be float32 [T, H]")
     _lib.check(_lib.load().vit_varlen_attn_planned(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), plan.items.data_ptr(),
-        plan.cap, plan.meta.data_ptr(), H, D, float(scale), dtype_code(q.dtype), out.data_ptr(),
-        _ptr(lse), _strides(q, k, v, out), _stream(q)))
+        plan.cap, plan.meta.data_ptr(), H, D, float(scale), dtype_code(q.dtype), _flags(causal),
+        out.data_ptr(), _ptr(lse), _strides(q, k, v, out), _stream(q)))
     return out
 
 

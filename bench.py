@@ -45,9 +45,14 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=2, help="seeded workload 1..5 (default 2)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--hook-every", type=int, default=8,
+                   help="time the attention kernel on every N-th step of the timed loop")
     p.add_argument("--causal", action="store_true",
                    help="causal variant (query a sees keys 0..a of its segment); FLOPs count "
                         "the unmasked pairs, 4*H*D*sum(s*(s+1)/2)")
+    p.add_argument("--fuse-q", action="store_true",
+                   help="q's RMSNorm + rotary inside the attention kernel; the pre-pass "
+                        "launch handles k only")
     p.add_argument("--dense-batch", action="store_true",
                    help="uniform workloads only: attention through vit_dense_batch_attn "
                         "(cu_seqlens = None form: no work-list, no metadata reads)")
@@ -234,6 +239,22 @@ def main():
                    float(wl.softmax_scale), dcode, flags, out.data_ptr(), None, strides_arr, sh)
         at_lse_args = at_args[:-3] + (lse_buf.data_ptr(), strides_arr, sh)
     f_fused = lib.vit_qk_norm_rope_worklist
+    if args.fuse_q:
+        if args.dense_batch:
+            sys.exit("bench: --fuse-q times the work-list step; drop --dense-batch")
+        # k's pre-pass with the work-list build in one launch; q's RMSNorm and
+        # rotary inside the attention kernel.
+        wk_p = wk.data_ptr() if wk is not None else None
+        wq_p = wq.data_ptr() if wq is not None else None
+        pre_args = (None, k.data_ptr(), T, H, D, dcode, pos.data_ptr(), float(wl.theta), None, wk_p,
+                    float(wl.eps), strides_arr, sh)
+        fused_args = pre_args[:11] + (0, strides_arr) + wl_args
+        f_at = lib.vit_varlen_attn_planned_qnorm_rope
+        at_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), cu.data_ptr(), plan.items.data_ptr(),
+                   plan.cap, plan.meta.data_ptr(), H, D, float(wl.softmax_scale), dcode, flags,
+                   pos.data_ptr(), float(wl.theta), wq_p, float(wl.eps), 0,
+                   out.data_ptr(), None, strides_arr, sh)
+        at_lse_args = at_args[:-3] + (lse_buf.data_ptr(), strides_arr, sh)
 
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -258,8 +279,11 @@ def main():
             e.record(stream)
         return evs
 
-    # e[0] / e[1]: the attention kernel's own dispatch start and end.
-    ev = [new_events(2) for _ in range(K)]
+    # e[0] / e[1]: the attention kernel's own dispatch start and end, taken on
+    # every hook_every-th step of the timed loop (a hooked launch records two
+    # more events, which adds a gap before the next launch).
+    every = max(1, args.hook_every)
+    ev = [new_events(2) if i % every == 0 else None for i in range(K)]
     torch.cuda.synchronize()
 
     def step(e=None):
@@ -283,27 +307,24 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / K
-    attn_avg_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    attn_avg_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev if e is not None]))
 
-    # Outside the timed region: the pre-pass and work-list kernels' own
-    # durations, from the same dispatch-timestamp events (each hooked launch
-    # adds a launch gap, so they are not hooked inside the timed loop).
-    side = [new_events(8) for _ in range(K)]
-    torch.cuda.synchronize()
-    for e in side:
-        check(f_hook(e[0].cuda_event, e[1].cuda_event))
-        check(f_pre(*pre_args))
-        check(f_hook(e[2].cuda_event, e[3].cuda_event))
-        check(f_wl(*wl_args))
-        check(f_hook(e[4].cuda_event, e[5].cuda_event))
-        check(f_fused(*fused_args))
-        check(f_hook(e[6].cuda_event, e[7].cuda_event))
-        check(f_at(*at_lse_args))
-    torch.cuda.synchronize()
-    pre_avg_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in side]))
-    wl_avg_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in side]))
-    fused_avg_ms = float(np.mean([e[4].elapsed_time(e[5]) for e in side]))
-    lse_avg_ms = float(np.mean([e[6].elapsed_time(e[7]) for e in side]))
+    # Outside the timed region: each other kernel's own duration, from the
+    # same dispatch-timestamp events, one kernel per loop (a kernel queued
+    # behind a different, still-running one would count part of its wait).
+    def side_loop(fn, fargs):
+        evs = [new_events(2) for _ in range(K)]
+        torch.cuda.synchronize()
+        for e in evs:
+            check(f_hook(e[0].cuda_event, e[1].cuda_event))
+            check(fn(*fargs))
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+
+    pre_avg_ms = side_loop(f_pre, pre_args)
+    wl_avg_ms = side_loop(f_wl, wl_args)
+    fused_avg_ms = side_loop(f_fused, fused_args)
+    lse_avg_ms = side_loop(f_at, at_lse_args)
 
     ceiling = mfma_ceiling(lib, torch, dev, stream) if is_bf16_dtype(wl) else None
 
@@ -330,7 +351,9 @@ def main():
                 traffic = tj.get("bytes_per_launch")
         except Exception:
             traffic = None
-    pre_bytes = 4 * T * H * D * (2 if is_bf16 else 4) + 8 * T + (8 * D if wl.use_norm else 0)
+    tensors = 1 if args.fuse_q else 2     # q and k, or k alone
+    pre_bytes = 2 * tensors * T * H * D * (2 if is_bf16 else 4) + 8 * T + \
+        (4 * tensors * D if wl.use_norm else 0)
     pre_gbps = pre_bytes / (pre_avg_ms * 1e-3) / 1e9
 
     result = {
@@ -348,7 +371,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name + ("_packed_qkv" if args.packed_qkv else "")
                    + ("_dense_batch" if args.dense_batch else "")
-                   + ("_causal" if args.causal else ""),
+                   + ("_causal" if args.causal else "")
+                   + ("_fused_q" if args.fuse_q else ""),
                    "images": wl.num_seqs, "tokens": T, "heads": H,
                    "head_dim": D, "max_seqlen": wl.max_seqlen, "qk_norm": wl.use_norm,
                    "rope": "2d", "flops_per_step": flops, "parallelism": "none (1 GPU)"},

@@ -91,11 +91,14 @@ enum vit_worklist_error {
  * rotary (_qkv_with_rope).  Arithmetic is fp32; results are rounded once to the
  * tensor dtype (nearest, ties to even).
  *
- *  q, k          [total_tokens, H, D] of `dtype`, updated in place.
+ *  q, k          [total_tokens, H, D] of `dtype`, updated in place.  q may be
+ *                NULL: only k is processed (q's half is then done inside the
+ *                attention by vit_varlen_attn_planned_qnorm_rope).
  *  pos           int32 [total_tokens, 2] (row, col); NULL = no rotary.
  *  theta         rotary base, finite and > 0 (10000 in the pages).
  *  q_weight,
- *  k_weight      fp32 [D]; both NULL = no norm; exactly one NULL is an error.
+ *  k_weight      fp32 [D]; both NULL = no norm; exactly one NULL is an error
+ *                (with q NULL: q_weight must be NULL, k_weight optional).
  *  eps           >= 0 (1e-6 in the pages).
  *  D             a multiple of 8 in [8, 256].
  * total_tokens == 0 is a no-op.
@@ -288,6 +291,29 @@ int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
                             const int32_t* meta, int num_heads, int head_dim, float scale,
                             int dtype, int flags, void* out, float* lse, const int64_t* strides,
                             hipStream_t stream);
+
+/*
+ * vit_varlen_attn_planned with the Q half of the pre-pass done inside the
+ * attention kernel: each work item stages its query rows in LDS, applies
+ * RMSNorm (q_weight, eps; null q_weight: none) and then the 2D rotary (pos,
+ * theta, rope_mode; null pos: none) as vit_qk_norm_rope_ex does to q, and
+ * feeds the result to the MFMAs.  q in memory is not modified.  This is
+ * _qkv_with_rope (vLLM page: norm, then rotary) with q's read and write of the
+ * separate pre-pass removed; k is still prepared by vit_qk_norm_rope_ex (or
+ * vit_qk_norm_rope_worklist) called with q = null.
+ *  pos        int32 [T, 2] (row, col), 8-byte aligned, or null.
+ *  q_weight   fp32 [D], 16-byte aligned, or null.
+ *  theta, eps, rope_mode   as for vit_qk_norm_rope_ex (checked when used).
+ * The rotary angle is reduced to a fraction of a turn exactly and evaluated
+ * with the hardware sine and cosine, so results match the separate pre-pass
+ * within the attention tolerance, not bit for bit.  Other arguments, layout
+ * and errors as for vit_varlen_attn_planned; head_dim at most 128.
+ */
+int vit_varlen_attn_planned_qnorm_rope(
+    const void* q, const void* k, const void* v, const int32_t* cu_seqlens, const int32_t* items,
+    int64_t cap, const int32_t* meta, int num_heads, int head_dim, float scale, int dtype,
+    int flags, const int32_t* pos, float theta, const float* q_weight, float eps, int rope_mode,
+    void* out, float* lse, const int64_t* strides, hipStream_t stream);
 
 /*
  * Reads (and with reset != 0 clears) the work-list error bits (enum

@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
                      "vit_time_next_kernel", "vit_probe_mfma", "vit_qk_norm_rope_worklist",
                      "vit_varlen_attn_lse", "vit_varlen_attn_strided",
                      "vit_qk_norm_rope_strided", "vit_dense_batch_attn", "vit_qk_norm_rope_ex",
-                     "vit_varlen_attn_ex"):
+                     "vit_varlen_attn_ex", "vit_varlen_attn_planned_qnorm_rope"):
         assert required in names
     assert sorted(_lib.SIGNATURES) == names
 
@@ -88,7 +88,12 @@ def test_attention_argument_errors(lib, args, code, needle):
 
 def test_prepass_argument_errors(lib):
     f = lib.vit_qk_norm_rope
-    assert f(None, FAKE, 4, 2, 64, 1, FAKE, 10000.0, None, None, 1e-6, None) == 1
+    assert f(FAKE, None, 4, 2, 64, 1, FAKE, 10000.0, None, None, 1e-6, None) == 1
+    assert "null k" in _err(lib)
+    # q may be null (k only), but then q_weight must be null too
+    assert f(None, FAKE, 4, 2, 64, 1, FAKE, 10000.0, FAKE, FAKE, 1e-6, None) == 1
+    assert "q_weight given without q" in _err(lib)
+    assert f(None, FAKE, 0, 2, 64, 1, FAKE, 10000.0, None, FAKE, 1e-6, None) == 0
     assert f(FAKE, FAKE + 0x100, 4, 2, 60, 1, FAKE, 10000.0, None, None, 1e-6, None) == 2
     assert f(FAKE, FAKE + 0x100, 4, 2, 64, 7, FAKE, 10000.0, None, None, 1e-6, None) == 1
     assert f(FAKE, FAKE + 0x100, 4, 2, 64, 1, FAKE, 10000.0, FAKE, None, 1e-6, None) == 1
@@ -166,8 +171,8 @@ def test_fused_prepass_worklist_checks_both_argument_sets(lib):
     meta = FAKE + 0x40
     ok_pre = (FAKE, FAKE + 0x1000, 16, 2, 64, 1, None, 1e4, None, None, 1e-6, 0, None)
     ok_wl = (FAKE, 3, 10, 64, FAKE, 3, meta, None)
-    assert f(None, *ok_pre[1:], *ok_wl) == _lib.VIT_ERR_INVALID_ARG          # pre-pass check
-    assert "q or k" in _err(lib)
+    assert f(ok_pre[0], None, *ok_pre[2:], *ok_wl) == _lib.VIT_ERR_INVALID_ARG  # pre-pass check
+    assert "null k" in _err(lib)
     bad_dim = ok_pre[:4] + (60,) + ok_pre[5:]
     assert f(*bad_dim, *ok_wl) == _lib.VIT_ERR_UNSUPPORTED
     assert f(*ok_pre, FAKE, 3, 200, 64, FAKE, 3, meta, None) == _lib.VIT_ERR_INVALID_ARG  # capacity
@@ -261,3 +266,22 @@ def test_attention_flags_are_checked(lib):
     planned = lib.vit_varlen_attn_planned
     assert planned(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1, 1, 8, FAKE + 0x100, None,
                    None, None) == _lib.VIT_ERR_INVALID_ARG
+
+
+def test_qnorm_rope_attention_argument_errors(lib):
+    f = lib.vit_varlen_attn_planned_qnorm_rope
+    head = (FAKE, FAKE + 0x100, FAKE + 0x200, FAKE, FAKE, 4, FAKE + 0x40, 2, 64, 0.1, 1, 0)
+    out = FAKE + 0x1000
+    ok_q = (FAKE, 1e4, FAKE, 1e-6, 0)     # pos, theta, q_weight, eps, rope_mode
+    bad = [((FAKE, 1e4, FAKE, 1e-6, 2), "rope_mode"),
+           ((FAKE + 4, 1e4, FAKE, 1e-6, 0), "pos must be 8-byte aligned"),
+           ((FAKE, 1e4, FAKE + 4, 1e-6, 0), "q_weight must be 16-byte aligned"),
+           ((FAKE, -1.0, FAKE, 1e-6, 0), "theta"),
+           ((FAKE, 1e4, FAKE, -1.0, 0), "eps")]
+    for qa, needle in bad:
+        assert f(*head, *qa, out, None, None, None) == _lib.VIT_ERR_INVALID_ARG
+        assert needle in _err(lib), needle
+    # the attention's own checks still apply
+    assert f(*head[:10], 7, *head[11:], *ok_q, out, None, None, None) == _lib.VIT_ERR_INVALID_ARG
+    # an empty plan is a no-op
+    assert f(*head[:5], 0, *head[6:], *ok_q, out, None, None, None) == _lib.VIT_OK

@@ -129,6 +129,11 @@ __device__ __forceinline__ float other_half(float x) {
   return __uint_as_float(threadIdx.x & 32 ? r[0] : r[1]);
 }
 
+__device__ __forceinline__ float bf16_bits_to_f32(u16 b) { return __uint_as_float(unsigned(b) << 16); }
+__device__ __forceinline__ u16 f32_to_bf16_bits(float x) {
+  return __builtin_bit_cast(u16, (__bf16)x);  // round to nearest even
+}
+
 __device__ __forceinline__ int swap_bits_2_3(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
     const int32_t* __restrict__ meta, int u_batch, int u_seq_len, int H, float scale_log2,
-    u16* __restrict__ out, float* __restrict__ lse, TokenStrides ts) {
+    u16* __restrict__ out, float* __restrict__ lse, TokenStrides ts, QPrepass qpre) {
   constexpr int D = C::D, BN = C::BN, KB = C::KB, STAGES = C::STAGES, NI = C::NI_HI, QB = C::QB;
   // When D is not a multiple of 32 the last 32-row block of O^T has padding
   // rows; row D then collects the row sums of P (see the tile loop), and
@@ -223,6 +228,25 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
                      : kPadOffset;
     cp_is_k[j] = is_k;
     cp_lds[j] = unsigned((is_k ? i * 64 : C::KREG + (i - C::NK) * 64) * 16);
+  }
+
+  // Q-side pre-pass (when asked for): the unit's query rows are staged in
+  // LDS, normalised and rotated there by all threads, then read back as the
+  // MFMA fragments.  The tables hold the norm weights and the rotary
+  // frequencies (turns per unit coordinate, hi + lo).
+  __shared__ __align__(16) u16 s_q[C::BM * D];
+  __shared__ float s_qw[D];
+  __shared__ float2 s_rev[kMaxQFreqs];
+  static_assert((C::LDS_BYTES + C::BM * D * 2 + D * 4 + kMaxQFreqs * 8) * C::OCC <= 160 * 1024,
+                "LDS budget with the Q staging rows");
+  const bool q_pending = qpre.pos != nullptr || qpre.weight != nullptr;
+  if (q_pending) {
+    for (int i = tid; i < D; i += C::THREADS) s_qw[i] = qpre.weight != nullptr ? qpre.weight[i] : 1.f;
+    if (tid == 0)
+      static_for<D / 4>([&](auto f_c) __attribute__((always_inline)) {
+        constexpr int f = decltype(f_c)::value;
+        s_rev[f] = make_float2(qpre.rev_hi[f], qpre.rev_lo[f]);
+      });
   }
 
   // items == null: a uniform batch (u_batch segments of u_seq_len tokens).
@@ -270,21 +294,105 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
                                   unsigned(((len - 1) * ts.v + D) * 2));
 
     // Q^T fragments (B operand of S^T = K Q^T): lane holds 8 dims of its row
-    // in each of the wave's QB query blocks.
+    // in each of the wave's QB query blocks: dims 16*st + 8*half + 0..7.
     bf16x8_t qf[QB][C::KSTEPS];
+    auto load_q = [&]() {
 #pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      const int row = row0 + 32 * b + l32;
-      if (row < len) {
-        const u16* qp = q + size_t(start + row) * ts.q + size_t(h) * D + half * 8;
+      for (int b = 0; b < QB; ++b) {
+        const int row = row0 + 32 * b + l32;
+        if (row < len) {
+          const u16* qp = q + size_t(start + row) * ts.q + size_t(h) * D + half * 8;
+#pragma unroll
+          for (int st = 0; st < C::KSTEPS; ++st)
+            qf[b][st] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qp + st * 16));
+        } else {
+#pragma unroll
+          for (int st = 0; st < C::KSTEPS; ++st) qf[b][st] = bf16x8_t{};
+        }
+      }
+    };
+    if (!q_pending) load_q();
+
+    // The Q-side pre-pass: RMSNorm then rotary in fp32, rounded once to bf16
+    // (the pre-pass kernel's arithmetic), on the unit's BM query rows staged
+    // in LDS.  Thread (r, hh) owns half hh of row r: its rotary pairs are
+    // (j, j + D/2) for j in [hh*D/4, (hh+1)*D/4) (rotate-half) or (2j, 2j+1)
+    // for the same j (complex), so a pair never spans two threads, and angle
+    // j uses the row coordinate for hh = 0 and the column coordinate for
+    // hh = 1 with frequency j - hh*D/4 in both modes.  Runtime loops keep
+    // the register footprint small next to the key loop's.
+    auto transform_q = [&]() {
+      constexpr int HALF = D / 2, QUART = D / 4;
+      const int qrows = min(C::BM, len - qt * C::BM);  // rows of this unit
+      const int r = tid >> 1, hh = tid & 1;
+      const int base_row = qt * C::BM;
+      u16* srow = s_q + r * D;
+      // 1. stage: each thread copies half a row (D bytes), zeros past the end
+      if (r < C::BM) {
+        const bool ok = r < qrows;
+        const u16* gq = q + size_t(start + base_row + (ok ? r : 0)) * ts.q + size_t(h) * D + hh * HALF;
+#pragma clang loop unroll(disable)
+        for (int c = 0; c < HALF; c += 8) {
+          const u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(gq + c) : u32x4_t{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4_t*>(srow + hh * HALF + c) = v;
+        }
+      }
+      __syncthreads();
+      // 2. scale (shared by the two threads of a row) and rotation
+      if (r < C::BM) {
+        const bool rope = qpre.pos != nullptr && r < qrows;
+        float rinv = 1.f;
+        if (qpre.weight != nullptr && r < qrows) {
+          float ss = 0.f;
+          // 16-byte reads: HALF is a multiple of 8 elements
+#pragma clang loop unroll(disable)
+          for (int c = 0; c < HALF; c += 8) {
+            const u32x4_t w4 = *reinterpret_cast<const u32x4_t*>(srow + hh * HALF + c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float lo = __uint_as_float(w4[i] << 16), hi = __uint_as_float(w4[i] & 0xffff0000u);
+              ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+            }
+          }
+          ss += __shfl_xor(ss, 1);
+          rinv = rsqrtf(ss * (1.f / D) + qpre.eps);
+        }
+        int2 pc = make_int2(0, 0);
+        if (rope) pc = *reinterpret_cast<const int2*>(qpre.pos + 2 * (start + base_row + r));
+        const float coord = float(hh ? pc.y : pc.x);
+        // QUART is a multiple of 4: four independent pairs per iteration keep
+        // their LDS reads and transcendentals overlapped.
+#pragma clang loop unroll_count(4)
+        for (int jj = 0; jj < QUART; ++jj) {
+          const int j = hh * QUART + jj;
+          // the pair's element indices
+          const int ia = qpre.rope_mode == 0 ? j : 2 * j;
+          const int ib = qpre.rope_mode == 0 ? j + HALF : 2 * j + 1;
+          const float a = bf16_bits_to_f32(srow[ia]) * rinv * s_qw[ia];
+          const float bb = bf16_bits_to_f32(srow[ib]) * rinv * s_qw[ib];
+          float ya = a, yb = bb;
+          if (rope) {
+            const float2 rv = s_rev[jj];
+            const float t = coord * rv.x;
+            const float frac = (t - rintf(t)) + (fmaf(coord, rv.x, -t) + coord * rv.y);
+            const float cs = __builtin_amdgcn_cosf(frac), sn = __builtin_amdgcn_sinf(frac);
+            ya = a * cs - bb * sn;
+            yb = bb * cs + a * sn;
+          }
+          srow[ia] = f32_to_bf16_bits(ya);
+          srow[ib] = f32_to_bf16_bits(yb);
+        }
+      }
+      __syncthreads();
+      // 3. fragments from the staged rows
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        const u16* sp = s_q + (wave * 32 * QB + 32 * b + l32) * D + half * 8;
 #pragma unroll
         for (int st = 0; st < C::KSTEPS; ++st)
-          qf[b][st] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qp + st * 16));
-      } else {
-#pragma unroll
-        for (int st = 0; st < C::KSTEPS; ++st) qf[b][st] = bf16x8_t{};
+          qf[b][st] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sp + st * 16));
       }
-    }
+    };
 
     // Reference max per query row (log2 domain), fixed for a whole pass over
     // the keys: p = 2^(s*c - m_ref) needs no rescaling of O, so the key loop
@@ -463,21 +571,28 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     };
 
     // One pass over the keys: tile 0 in mode M0, the others in mode M.
-    auto run_pass = [&](auto m0_tag, auto m_tag) {
+    // The previous unit's (or pass's) last tile must no longer be read, then
+    // the pass's first tiles are issued.  The Q loads may still be in flight:
+    // loads complete in issue order, so a copy wait (vmcnt) also covers the
+    // older Q loads, and the first tiles' copies overlap them.
+    auto start_pass = [&]() {
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < STAGES - 1; ++t)
+        if (t < ntiles) issue_tile(t);
+    };
+    start_pass();
+    // The Q-side pre-pass, while the first tiles are in flight.
+    if (q_pending) transform_q();
+
+    auto run_pass = [&](auto m0_tag, auto m_tag, bool started) {
+      if (!started) start_pass();
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
 #pragma unroll
         for (int d = 0; d < C::DB; ++d) o[b][d] = f32x16_t{};
         l_run[b] = 0.f;  // this lane's partial row sum
       }
-      // The previous unit's (or pass's) last tile must no longer be read.
-      // The Q loads may still be in flight: loads complete in issue order, so
-      // a copy wait (vmcnt) also covers the older Q loads, and the first
-      // tile's copies overlap them.
-      __syncthreads();
-#pragma unroll
-      for (int t = 0; t < STAGES - 1; ++t)
-        if (t < ntiles) issue_tile(t);
       // Tiles before nfull need no mask: every key is inside the segment and
       // (causal) at or before the unit's first query row.  The rest are masked.
       const int nfull = CAUSAL ? min(len, qt * C::BM + 1) / BN : len / BN;
@@ -490,7 +605,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       for (int t = nfull > 1 ? nfull : 1; t < ntiles; ++t) process_tile(std::true_type{}, m_tag, t);
     };
 
-    run_pass(std::integral_constant<int, kSetRef>{}, std::integral_constant<int, kPlain>{});
+    run_pass(std::integral_constant<int, kSetRef>{}, std::integral_constant<int, kPlain>{}, true);
     bool repeat = false;
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
@@ -499,10 +614,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     }
     // Every wave shares the copy ring, so the workgroup repeats together.
     if (__syncthreads_or(repeat)) {
-      run_pass(std::integral_constant<int, kMaxOnly>{}, std::integral_constant<int, kMaxOnly>{});
+      run_pass(std::integral_constant<int, kMaxOnly>{}, std::integral_constant<int, kMaxOnly>{}, false);
 #pragma unroll
       for (int b = 0; b < QB; ++b) m_ref[b] = m_seen[b];
-      run_pass(std::integral_constant<int, kPlain>{}, std::integral_constant<int, kPlain>{});
+      run_pass(std::integral_constant<int, kPlain>{}, std::integral_constant<int, kPlain>{}, false);
     }
 
     // Finalize: O^T register r of block d holds dim 32d + 8(r>>2) + 4half + (r&3).
@@ -537,8 +652,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
 
 template <class C>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, const Schedule& sch, int H,
-                      float scale, bool causal, void* out, float* lse, TokenStrides ts,
-                      hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+                      float scale, bool causal, const QPrepass* qp, void* out, float* lse,
+                      TokenStrides ts, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+  QPrepass qpre{};
+  if (qp != nullptr) qpre = *qp;
   const int64_t items = sch.items != nullptr
                             ? sch.cap
                             : int64_t(sch.batch) * ((sch.seq_len + C::BM - 1) / C::BM);
@@ -551,7 +668,7 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const Schedul
   hipExtLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), 0, stream, e0, e1, 0,
                      static_cast<const u16*>(q), static_cast<const u16*>(k),
                      static_cast<const u16*>(v), sch.cu, sch.items, sch.meta, sch.batch,
-                     sch.seq_len, H, c, static_cast<u16*>(out), lse, ts);
+                     sch.seq_len, H, c, static_cast<u16*>(out), lse, ts, qpre);
   return hipGetLastError();
 }
 
@@ -566,24 +683,25 @@ template <> struct Choice<128> { using C = Cfg<128, 4, 1, 32, 2, 2>; };
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, const Schedule& sch, int H,
-                    float scale, bool causal, void* out, float* lse, TokenStrides ts,
-                    hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+                    float scale, bool causal, const QPrepass* qp, void* out, float* lse,
+                    TokenStrides ts, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   using C = typename Choice<D>::C;
   static_assert(C::BM == bf16_block_m_const(D), "work-list block size mismatch");
-  return launch_cfg<C>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
+  return launch_cfg<C>(q, k, v, sch, H, scale, causal, qp, out, lse, ts, stream, e0, e1);
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const Schedule& sch,
-                            int H, int D, float scale, bool causal, void* out, float* lse,
-                            TokenStrides ts, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+                            int H, int D, float scale, bool causal, const QPrepass* qp, void* out,
+                            float* lse, TokenStrides ts, hipStream_t stream, hipEvent_t e0,
+                            hipEvent_t e1) {
   switch (D) {
-    case 32: return launch_d<32>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
-    case 64: return launch_d<64>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
-    case 80: return launch_d<80>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
-    case 96: return launch_d<96>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
-    case 128: return launch_d<128>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
+    case 32: return launch_d<32>(q, k, v, sch, H, scale, causal, qp, out, lse, ts, stream, e0, e1);
+    case 64: return launch_d<64>(q, k, v, sch, H, scale, causal, qp, out, lse, ts, stream, e0, e1);
+    case 80: return launch_d<80>(q, k, v, sch, H, scale, causal, qp, out, lse, ts, stream, e0, e1);
+    case 96: return launch_d<96>(q, k, v, sch, H, scale, causal, qp, out, lse, ts, stream, e0, e1);
+    case 128: return launch_d<128>(q, k, v, sch, H, scale, causal, qp, out, lse, ts, stream, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

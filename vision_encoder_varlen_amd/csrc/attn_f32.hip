@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
     const int32_t* __restrict__ meta, int u_batch, int u_seq_len, int H, float scale,
-    float* __restrict__ out, float* __restrict__ lse, TokenStrides ts) {
+    float* __restrict__ out, float* __restrict__ lse, TokenStrides ts, QPrepass qpre) {
   constexpr int HD = D / 2;
   constexpr int ROW = D + 4;  // +16 bytes per LDS row
   __shared__ __align__(16) float ks[kBN * ROW];
@@ -74,6 +74,55 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
     } else {
 #pragma unroll
       for (int d = 0; d < HD; ++d) qv[d] = 0.f;
+    }
+    // Q-side pre-pass (RMSNorm then rotary, fp32).  This lane holds dims
+    // half * D/2 + d: rotate-half partners sit in the other half of the wave
+    // at the same d; complex partners are d ^ 1 in this lane.
+    if (qpre.weight != nullptr) {
+      float ss = 0.f;
+#pragma unroll
+      for (int d = 0; d < HD; ++d) ss = fmaf(qv[d], qv[d], ss);
+      ss += __shfl_xor(ss, 32);
+      const float rinv = rsqrtf(ss * (1.f / D) + qpre.eps);
+#pragma unroll
+      for (int d = 0; d < HD; ++d) qv[d] = qv[d] * rinv * qpre.weight[half * HD + d];
+    }
+    if (qpre.pos != nullptr) {
+      int2 pr = make_int2(0, 0);
+      if (qrow < len) pr = *reinterpret_cast<const int2*>(qpre.pos + 2 * (start + qrow));
+      // Angle of frequency F on the row (col = false) or column axis:
+      // 2*pi * coord * rev[F], reduced to a fraction of a turn exactly, then an
+      // accurate sincosf.  F is a compile-time constant (no dynamic indexing
+      // of the parameter block).
+      auto cos_sin = [&](auto f_c, bool col) {
+        constexpr int F = decltype(f_c)::value;
+        const float c = float(col ? pr.y : pr.x);
+        const float t = c * qpre.rev_hi[F];
+        const float frac = (t - rintf(t)) + (fmaf(c, qpre.rev_hi[F], -t) + c * qpre.rev_lo[F]);
+        float sn, cn;
+        sincosf(6.283185307179586f * frac, &sn, &cn);
+        return make_float2(cn, sn);
+      };
+      if (qpre.rope_mode == 0) {
+        // pair index j = d for both halves
+        static_for<HD>([&](auto d_c) {
+          constexpr int d = decltype(d_c)::value;
+          const float part = __shfl_xor(qv[d], 32);
+          const float2 cs = cos_sin(std::integral_constant<int, (d < D / 4 ? d : d - D / 4)>{},
+                                    d >= D / 4);
+          qv[d] = half == 0 ? qv[d] * cs.x - part * cs.y : qv[d] * cs.x + part * cs.y;
+        });
+      } else {
+        // pair index j = half * D/4 + d/2: the row axis in half 0, the column
+        // axis in half 1, frequency d/2 in both
+        static_for<HD / 2>([&](auto i_c) {
+          constexpr int d = 2 * decltype(i_c)::value;
+          const float2 cs = cos_sin(std::integral_constant<int, d / 2>{}, half != 0);
+          const float a = qv[d], b = qv[d + 1];
+          qv[d] = a * cs.x - b * cs.y;
+          qv[d + 1] = b * cs.x + a * cs.y;
+        });
+      }
     }
     float m = -INFINITY, l = 0.f;
     // Keys visited: the segment, or with CAUSAL those up to the unit's last row.
@@ -130,8 +179,10 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, const Schedule& sch, int H,
-                    float scale, bool causal, void* out, float* lse, TokenStrides ts,
-                    hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+                    float scale, bool causal, const QPrepass* qp, void* out, float* lse,
+                    TokenStrides ts, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+  QPrepass qpre{};
+  if (qp != nullptr) qpre = *qp;
   const int64_t items = sch.items != nullptr
                             ? sch.cap
                             : int64_t(sch.batch) * ((sch.seq_len + kBM - 1) / kBM);
@@ -142,21 +193,22 @@ hipError_t launch_d(const void* q, const void* k, const void* v, const Schedule&
   hipExtLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), 0, stream, e0, e1, 0,
                      static_cast<const float*>(q), static_cast<const float*>(k),
                      static_cast<const float*>(v), sch.cu, sch.items, sch.meta, sch.batch,
-                     sch.seq_len, H, scale, static_cast<float*>(out), lse, ts);
+                     sch.seq_len, H, scale, static_cast<float*>(out), lse, ts, qpre);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const Schedule& sch,
-                           int H, int D, float scale, bool causal, void* out, float* lse,
-                           TokenStrides ts, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+                           int H, int D, float scale, bool causal, const QPrepass* qp, void* out,
+                           float* lse, TokenStrides ts, hipStream_t stream, hipEvent_t e0,
+                           hipEvent_t e1) {
   switch (D) {
-    case 32: return launch_d<32>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
-    case 64: return launch_d<64>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
-    case 80: return launch_d<80>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
-    case 96: return launch_d<96>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
-    case 128: return launch_d<128>(q, k, v, sch, H, scale, causal, out, lse, ts, stream, e0, e1);
+    case 32: return launch_d<32>(q, k, v, sch, H, scale, causal, qp, out, lse, ts, stream, e0, e1);
+    case 64: return launch_d<64>(q, k, v, sch, H, scale, causal, qp, out, lse, ts, stream, e0, e1);
+    case 80: return launch_d<80>(q, k, v, sch, H, scale, causal, qp, out, lse, ts, stream, e0, e1);
+    case 96: return launch_d<96>(q, k, v, sch, H, scale, causal, qp, out, lse, ts, stream, e0, e1);
+    case 128: return launch_d<128>(q, k, v, sch, H, scale, causal, qp, out, lse, ts, stream, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

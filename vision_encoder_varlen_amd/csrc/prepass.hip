@@ -125,7 +125,8 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
   const int half_d = D / 2;
   const int quarter_d = D / 4;
   const bool rope = pos != nullptr;
-  const bool norm = wq != nullptr;
+  const bool norm = wk != nullptr;    // wq too, when q is given
+  const bool has_q = q != nullptr;    // null: k only (q is rotated elsewhere)
   const float inv_d = 1.f / float(D);
 
   // A row takes G consecutive lanes of a wave; a wave holds 64 / G rows.
@@ -142,8 +143,8 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
   if (norm && lane_active) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      wa[0][e] = wq[m0 + e];
-      wb[0][e] = wq[m0 + half_d + e];
+      wa[0][e] = has_q ? wq[m0 + e] : 0.f;
+      wb[0][e] = has_q ? wq[m0 + half_d + e] : 0.f;
       wa[1][e] = wk[m0 + e];
       wb[1][e] = wk[m0 + half_d + e];
     }
@@ -183,8 +184,10 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
       // keeps four independent loads in flight.
       float a[2][E] = {}, b[2][E] = {};
       if (row_ok) {
-        loadE<E>(q + qbase + m0, a[0]);
-        loadE<E>(q + qbase + m0 + half_d, b[0]);
+        if (has_q) {
+          loadE<E>(q + qbase + m0, a[0]);
+          loadE<E>(q + qbase + m0 + half_d, b[0]);
+        }
         loadE<E>(k + kbase + m0, a[1]);
         loadE<E>(k + kbase + m0 + half_d, b[1]);
       }
@@ -244,8 +247,10 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
         }
       }
       if (row_ok) {
-        storeE<E>(q + qbase + m0, a[0]);
-        storeE<E>(q + qbase + m0 + half_d, b[0]);
+        if (has_q) {
+          storeE<E>(q + qbase + m0, a[0]);
+          storeE<E>(q + qbase + m0 + half_d, b[0]);
+        }
         storeE<E>(k + kbase + m0, a[1]);
         storeE<E>(k + kbase + m0 + half_d, b[1]);
       }
@@ -265,7 +270,7 @@ hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
   const int ks = k_stride > 0 ? k_stride : H * D;
   WorklistJob jb{};
   if (job != nullptr) jb = *job;
-  const bool prepass_work = T > 0 && (pos != nullptr || wq != nullptr);
+  const bool prepass_work = T > 0 && (pos != nullptr || wk != nullptr);
   if (!prepass_work) {
     if (jb.cu == nullptr) return hipSuccess;
     return launch_worklist(jb.cu, jb.N, jb.max_seqlen, jb.block_m, jb.items, jb.cap, jb.meta,

@@ -141,15 +141,47 @@ int check_flags(int flags) {
 
 int launch_attn(const void* q, const void* k, const void* v, const vit::Schedule& sch, int H,
                 int D, float scale, int dtype, int flags, void* out, float* lse,
-                const vit::TokenStrides& ts, hipStream_t stream, const TimingHook& t) {
+                const vit::TokenStrides& ts, hipStream_t stream, const TimingHook& t,
+                const vit::QPrepass* qp = nullptr) {
   const bool causal = (flags & VIT_ATTN_CAUSAL) != 0;
   const hipError_t e =
       dtype == VIT_BF16
-          ? vit::launch_attn_bf16(q, k, v, sch, H, D, scale, causal, out, lse, ts, stream, t.start,
-                                  t.stop)
-          : vit::launch_attn_f32(q, k, v, sch, H, D, scale, causal, out, lse, ts, stream, t.start,
-                                 t.stop);
+          ? vit::launch_attn_bf16(q, k, v, sch, H, D, scale, causal, qp, out, lse, ts, stream,
+                                  t.start, t.stop)
+          : vit::launch_attn_f32(q, k, v, sch, H, D, scale, causal, qp, out, lse, ts, stream,
+                                 t.start, t.stop);
   return e == hipSuccess ? ok() : hip_fail(e, "attention launch");
+}
+
+// Q-side pre-pass parameters for the attention kernels: the same rotary
+// frequencies as the pre-pass (theta^(-2j/(D/2)), double), divided by 2*pi
+// and split into float hi + lo.
+int make_qprepass(int D, const int32_t* pos, float theta, const float* q_weight, float eps,
+                  int rope_mode, vit::QPrepass* qp) {
+  if (rope_mode != VIT_ROPE_NEOX && rope_mode != VIT_ROPE_COMPLEX)
+    return fail(VIT_ERR_INVALID_ARG, "unknown rope_mode %d", rope_mode);
+  if (pos != nullptr && (!std::isfinite(theta) || theta <= 0.f))
+    return fail(VIT_ERR_INVALID_ARG, "theta must be finite and > 0");
+  if (q_weight != nullptr && (!std::isfinite(eps) || eps < 0.f))
+    return fail(VIT_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (pos != nullptr && (reinterpret_cast<uintptr_t>(pos) & 7u) != 0)
+    return fail(VIT_ERR_INVALID_ARG, "pos must be 8-byte aligned");
+  if (q_weight != nullptr && !aligned16(q_weight))
+    return fail(VIT_ERR_INVALID_ARG, "q_weight must be 16-byte aligned");
+  *qp = vit::QPrepass{};
+  qp->pos = pos;
+  qp->weight = q_weight;
+  qp->eps = eps;
+  qp->rope_mode = rope_mode;
+  if (pos != nullptr) {
+    const double two_pi = 6.283185307179586476925286766559;
+    for (int j = 0; j < D / 4; ++j) {
+      const double rev = std::pow(double(theta), -2.0 * j / (D / 2.0)) / two_pi;
+      qp->rev_hi[j] = float(rev);
+      qp->rev_lo[j] = float(rev - double(qp->rev_hi[j]));
+    }
+  }
+  return VIT_OK;
 }
 
 // Token strides (elements) of q, k, v, out from a caller array of n values
@@ -222,7 +254,7 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, 
 int check_prepass_args(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
                        int dtype, const int32_t* pos, float theta, const float* q_weight,
                        const float* k_weight, float eps, int rope_mode) {
-  if (!q || !k) return fail(VIT_ERR_INVALID_ARG, "null q or k");
+  if (!k) return fail(VIT_ERR_INVALID_ARG, "null k (q may be null, k may not)");
   if (rope_mode != VIT_ROPE_NEOX && rope_mode != VIT_ROPE_COMPLEX)
     return fail(VIT_ERR_INVALID_ARG, "unknown rope_mode %d", rope_mode);
   if (total_tokens < 0) return fail(VIT_ERR_INVALID_ARG, "total_tokens must be >= 0");
@@ -230,14 +262,16 @@ int check_prepass_args(void* q, void* k, int64_t total_tokens, int num_heads, in
   if (head_dim < 8 || head_dim > 256 || head_dim % 8 != 0)
     return fail(VIT_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 in [8, 256] (got %d)", head_dim);
   if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-  if ((q_weight == nullptr) != (k_weight == nullptr))
+  if (q == nullptr && q_weight != nullptr)
+    return fail(VIT_ERR_INVALID_ARG, "q_weight given without q");
+  if (q != nullptr && (q_weight == nullptr) != (k_weight == nullptr))
     return fail(VIT_ERR_INVALID_ARG, "give both q_weight and k_weight or neither");
   if (pos != nullptr && (!std::isfinite(theta) || theta <= 0.f))
     return fail(VIT_ERR_INVALID_ARG, "theta must be finite and > 0");
-  if (q_weight != nullptr && (!std::isfinite(eps) || eps < 0.f))
+  if (k_weight != nullptr && (!std::isfinite(eps) || eps < 0.f))
     return fail(VIT_ERR_INVALID_ARG, "eps must be finite and >= 0");
   if (!aligned16(q) || !aligned16(k)) return fail(VIT_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
-  if (q_weight && (!aligned16(q_weight) || !aligned16(k_weight)))
+  if ((q_weight && !aligned16(q_weight)) || (k_weight && !aligned16(k_weight)))
     return fail(VIT_ERR_INVALID_ARG, "norm weights must be 16-byte aligned");
   if (pos && !aligned4(pos)) return fail(VIT_ERR_INVALID_ARG, "pos must be 4-byte aligned");
   if (q == k) return fail(VIT_ERR_INVALID_ARG, "q and k must be distinct buffers");
@@ -269,7 +303,7 @@ int launch_prepass_job(void* q, void* k, int64_t total_tokens, int num_heads, in
                        const float* k_weight, float eps, int rope_mode,
                        const vit::WorklistJob* job, const vit::TokenStrides& ts,
                        hipStream_t stream, const TimingHook& t) {
-  const bool prepass_work = total_tokens > 0 && (pos != nullptr || q_weight != nullptr);
+  const bool prepass_work = total_tokens > 0 && (pos != nullptr || k_weight != nullptr);
   if (!prepass_work && job == nullptr) {
     const hipError_t e = record_empty(t, stream);
     return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
@@ -426,6 +460,35 @@ int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
   }
   return launch_attn(q, k, v, vit::Schedule{cu_seqlens, items, meta, cap, 0, 0}, num_heads,
                      head_dim, scale, dtype, flags, out, lse, ts, stream, t);
+}
+
+int vit_varlen_attn_planned_qnorm_rope(
+    const void* q, const void* k, const void* v, const int32_t* cu_seqlens, const int32_t* items,
+    int64_t cap, const int32_t* meta, int num_heads, int head_dim, float scale, int dtype,
+    int flags, const int32_t* pos, float theta, const float* q_weight, float eps, int rope_mode,
+    void* out, float* lse, const int64_t* strides, hipStream_t stream) {
+  const TimingHook t = take_timing();
+  if (!items || !meta) return fail(VIT_ERR_INVALID_ARG, "null work-list pointer");
+  if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  int rc = check_attn_args(q, k, v, cu_seqlens, 0, 0, num_heads, head_dim, scale, out);
+  if (rc != VIT_OK) return rc;
+  rc = check_flags(flags);
+  if (rc != VIT_OK) return rc;
+  if (cap < 0 || cap > kMaxCapacity) return fail(VIT_ERR_INVALID_ARG, "bad work-list capacity %lld", (long long)cap);
+  rc = check_lse(lse, q, k, v, out);
+  if (rc != VIT_OK) return rc;
+  vit::TokenStrides ts{};
+  rc = make_strides(strides, 4, num_heads, head_dim, dtype, &ts);
+  if (rc != VIT_OK) return rc;
+  vit::QPrepass qp{};
+  rc = make_qprepass(head_dim, pos, theta, q_weight, eps, rope_mode, &qp);
+  if (rc != VIT_OK) return rc;
+  if (cap == 0) {
+    const hipError_t e = record_empty(t, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
+  }
+  return launch_attn(q, k, v, vit::Schedule{cu_seqlens, items, meta, cap, 0, 0}, num_heads,
+                     head_dim, scale, dtype, flags, out, lse, ts, stream, t, &qp);
 }
 
 int vit_dense_batch_attn(const void* q, const void* k, const void* v, int batch, int seq_len,

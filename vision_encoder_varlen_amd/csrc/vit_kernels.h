@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace vit {
 
 // Elements between consecutive tokens of each tensor ([T, H, D] contiguous:
@@ -12,6 +15,34 @@ namespace vit {
 // token's heads stay contiguous (head h at offset h * D).
 struct TokenStrides {
   int q, k, v, o;
+};
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1: a loop whose
+// index is a compile-time constant in the body (array indices stay constant,
+// so nothing indexed by it is placed in scratch memory).
+template <class F, int... I>
+__host__ __device__ __attribute__((always_inline)) inline void static_for_impl(
+    F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__host__ __device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Q-side pre-pass applied by the attention kernels to each query row as they
+// load it (pos == null and weight == null: none).  The rotation angle of pair
+// index j for coordinate c is 2*pi * c * rev[j] with rev[j] = inv_freq[j] /
+// (2*pi) held as an unevaluated sum rev_hi[j] + rev_lo[j], so the angle can be
+// reduced to a fraction of a turn exactly before the hardware sine and cosine.
+constexpr int kMaxQFreqs = 32;  // D/4 for D <= 128
+struct QPrepass {
+  const int32_t* pos;    // int32 [T, 2] (row, col), or null: no rotary
+  const float* weight;   // fp32 [D] RMSNorm weight, or null: no norm
+  float eps;
+  int rope_mode;         // 0: rotate-half pairs (m, m + D/2); 1: pairs (2j, 2j + 1)
+  float rev_hi[kMaxQFreqs];
+  float rev_lo[kMaxQFreqs];
 };
 
 // Where the attention kernels take their (segment, q-tile) items from: a
@@ -90,14 +121,15 @@ hipError_t launch_worklist(const int32_t* cu, int N, int max_seqlen, int block_m
                            hipEvent_t ev_start, hipEvent_t ev_stop);
 
 // causal: query row a of a segment sees keys 0..a of that segment only.
+// qp: optional Q-side pre-pass (null: q is used as stored).
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const Schedule& sch,
-                            int H, int D, float scale, bool causal, void* out, float* lse,
-                            TokenStrides ts, hipStream_t stream, hipEvent_t ev_start,
+                            int H, int D, float scale, bool causal, const QPrepass* qp, void* out,
+                            float* lse, TokenStrides ts, hipStream_t stream, hipEvent_t ev_start,
                             hipEvent_t ev_stop);
 
 hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const Schedule& sch,
-                           int H, int D, float scale, bool causal, void* out, float* lse,
-                           TokenStrides ts, hipStream_t stream, hipEvent_t ev_start,
+                           int H, int D, float scale, bool causal, const QPrepass* qp, void* out,
+                           float* lse, TokenStrides ts, hipStream_t stream, hipEvent_t ev_start,
                            hipEvent_t ev_stop);
 
 // Attention launches: lse (fp32 [T, H], may be null) receives each row's

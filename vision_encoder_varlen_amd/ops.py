@@ -48,6 +48,11 @@ def _strides(*ts: torch.Tensor):
     return (ctypes.c_int64 * len(vals))(*vals)
 
 
+def _strides_qk(q, k):
+    """Token strides of (q, k) for the pre-pass; q may be None (k only)."""
+    return _strides(k, k) if q is None else _strides(q, k)
+
+
 def dtype_code(dtype: torch.dtype) -> int:
     if dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {dtype}; expected float32 or bfloat16")
@@ -55,11 +60,12 @@ def dtype_code(dtype: torch.dtype) -> int:
 
 
 def _prepass_checks(q, k, pos, q_weight, k_weight) -> None:
-    _need_cuda("q", q, token_strided=True)
-    _need_cuda("k", k, q.dtype, token_strided=True)
-    if q.dim() != 3 or k.shape != q.shape:
+    if q is not None:
+        _need_cuda("q", q, token_strided=True)
+    _need_cuda("k", k, None if q is None else q.dtype, token_strided=True)
+    if k.dim() != 3 or (q is not None and k.shape != q.shape):
         raise ValueError("q and k must both be [T, H, D]")
-    T, H, D = q.shape
+    T, H, D = k.shape
     if pos is not None:
         _need_cuda("pos", pos, torch.int32)
         if pos.shape != (T, 2):
@@ -86,13 +92,14 @@ def qk_norm_rope_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch.Tensor] 
                   rope_mode: str = "neox") -> None:
     """In-place Q/K RMSNorm (when weights are given) then 2D rotary (when ``pos`` is given).
 
-    ``rope_mode``: ``"neox"`` pairs ``(m, m + D/2)``; ``"complex"`` pairs ``(2j, 2j + 1)``."""
+    ``rope_mode``: ``"neox"`` pairs ``(m, m + D/2)``; ``"complex"`` pairs ``(2j, 2j + 1)``.
+    ``q`` may be None (k only; q's half then runs inside ``varlen_attn_planned_qnorm_rope``)."""
     _prepass_checks(q, k, pos, q_weight, k_weight)
-    T, H, D = q.shape
+    T, H, D = k.shape
     _lib.check(_lib.load().vit_qk_norm_rope_ex(
-        q.data_ptr(), k.data_ptr(), T, H, D, dtype_code(q.dtype), _ptr(pos), float(theta),
-        _ptr(q_weight), _ptr(k_weight), float(eps), _rope_mode(rope_mode), _strides(q, k),
-        _stream(q)))
+        _ptr(q), k.data_ptr(), T, H, D, dtype_code(k.dtype), _ptr(pos), float(theta),
+        _ptr(q_weight), _ptr(k_weight), float(eps), _rope_mode(rope_mode), _strides_qk(q, k),
+        _stream(k)))
 
 
 def qk_norm_rope_worklist_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch.Tensor],
@@ -104,13 +111,13 @@ def qk_norm_rope_worklist_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch
     _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
     if cu_seqlens.numel() - 1 != plan.num_seqs:
         raise ValueError("cu_seqlens does not match the plan")
-    T, H, D = q.shape
+    T, H, D = k.shape
     _lib.check(_lib.load().vit_qk_norm_rope_worklist(
-        q.data_ptr(), k.data_ptr(), T, H, D, dtype_code(q.dtype), _ptr(pos), float(theta),
-        _ptr(q_weight), _ptr(k_weight), float(eps), _rope_mode(rope_mode), _strides(q, k),
+        _ptr(q), k.data_ptr(), T, H, D, dtype_code(k.dtype), _ptr(pos), float(theta),
+        _ptr(q_weight), _ptr(k_weight), float(eps), _rope_mode(rope_mode), _strides_qk(q, k),
         cu_seqlens.data_ptr(), plan.num_seqs,
         plan.max_seqlen, plan.block_m, plan.items.data_ptr(), plan.cap, plan.meta.data_ptr(),
-        _stream(q)))
+        _stream(k)))
     return plan
 
 
@@ -277,6 +284,48 @@ def varlen_attn_planned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _lib.check(_lib.load().vit_varlen_attn_planned(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), plan.items.data_ptr(),
         plan.cap, plan.meta.data_ptr(), H, D, float(scale), dtype_code(q.dtype), _flags(causal),
+        out.data_ptr(), _ptr(lse), _strides(q, k, v, out), _stream(q)))
+    return out
+
+
+def varlen_attn_planned_qnorm_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                   cu_seqlens: torch.Tensor, plan: Plan,
+                                   pos: Optional[torch.Tensor], theta: float = 10000.0,
+                                   q_weight: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                                   rope_mode: str = "neox", scale: Optional[float] = None,
+                                   out: Optional[torch.Tensor] = None,
+                                   lse: Optional[torch.Tensor] = None,
+                                   causal: bool = False) -> torch.Tensor:
+    """``varlen_attn_planned`` with q's RMSNorm + rotary applied inside the kernel
+    (``q`` itself is left unchanged); prepare ``k`` with ``qk_norm_rope_(None, k, ...)``."""
+    _attn_checks(q, k, v, cu_seqlens)
+    T, H, D = q.shape
+    if plan.block_m != attn_block_m(H, D, q.dtype):
+        raise ValueError("plan was built with a different block_m than this kernel uses")
+    if pos is not None:
+        _need_cuda("pos", pos, torch.int32)
+        if pos.shape != (T, 2):
+            raise ValueError("pos must be int32 [T, 2]")
+    if q_weight is not None:
+        _need_cuda("q_weight", q_weight, torch.float32)
+        if q_weight.shape != (D,):
+            raise ValueError("q_weight must be float32 [D]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_cuda("out", out, q.dtype, token_strided=True)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if lse is not None:
+        _need_cuda("lse", lse, torch.float32)
+        if lse.shape != (T, H):
+            raise ValueError("lse must be float32 [T, H]")
+    _lib.check(_lib.load().vit_varlen_attn_planned_qnorm_rope(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), plan.items.data_ptr(),
+        plan.cap, plan.meta.data_ptr(), H, D, float(scale), dtype_code(q.dtype), _flags(causal),
+        _ptr(pos), float(theta), _ptr(q_weight), float(eps), _rope_mode(rope_mode),
         out.data_ptr(), _ptr(lse), _strides(q, k, v, out), _stream(q)))
     return out
 

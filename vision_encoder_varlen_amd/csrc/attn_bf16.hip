@@ -661,7 +661,7 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const Schedul
                             : int64_t(sch.batch) * ((sch.seq_len + C::BM - 1) / C::BM);
   const int64_t units = items * int64_t(H);
   if (units <= 0) return hipSuccess;
-  const int64_t grid = units < kMaxAttnGrid ? units : kMaxAttnGrid;
+  const int64_t grid = units < kMaxAttnGridBf16 ? units : kMaxAttnGridBf16;
   const float c = scale * kLog2e;
   auto kern = causal ? (c > 0.f ? attn_bf16_kernel<C, true, true> : attn_bf16_kernel<C, false, true>)
                     : (c > 0.f ? attn_bf16_kernel<C, true, false> : attn_bf16_kernel<C, false, false>);

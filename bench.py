@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=2, help="seeded workload 1..5 (default 2)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--hook-every", type=int, default=1,
+    p.add_argument("--hook-every", type=int, default=8,
                    help="time the attention kernel on every N-th step of the timed loop")
     p.add_argument("--causal", action="store_true",
                    help="causal variant (query a sees keys 0..a of its segment); FLOPs count "

@@ -232,13 +232,16 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
 
   // Q-side pre-pass (when asked for): the unit's query rows are staged in
   // LDS, normalised and rotated there by all threads, then read back as the
-  // MFMA fragments.  The tables hold the norm weights and the rotary
-  // frequencies (turns per unit coordinate, hi + lo).
-  __shared__ __align__(16) u16 s_q[C::BM * D];
+  // MFMA fragments.  The staging rows reuse the K/V ring, which is idle then
+  // (the unit's first tiles are issued after the transform).  The tables
+  // hold the norm weights and the rotary frequencies (turns per unit
+  // coordinate, hi + lo).
+  u16* const s_q = smem;
+  static_assert(C::BM * D * 2 <= C::LDS_BYTES, "Q staging rows must fit in the K/V ring");
   __shared__ float s_qw[D];
   __shared__ float2 s_rev[kMaxQFreqs];
-  static_assert((C::LDS_BYTES + C::BM * D * 2 + D * 4 + kMaxQFreqs * 8) * C::OCC <= 160 * 1024,
-                "LDS budget with the Q staging rows");
+  static_assert((C::LDS_BYTES + D * 4 + kMaxQFreqs * 8) * C::OCC <= 160 * 1024,
+                "LDS budget with the pre-pass tables");
   const bool q_pending = qpre.pos != nullptr || qpre.weight != nullptr;
   if (q_pending) {
     for (int i = tid; i < D; i += C::THREADS) s_qw[i] = qpre.weight != nullptr ? qpre.weight[i] : 1.f;
@@ -254,10 +257,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
   const int uni_tiles = (u_seq_len + C::BM - 1) / C::BM;
   const int64_t nunits = (uniform ? int64_t(u_batch) * uni_tiles : int64_t(meta[0])) * H;
   for (int64_t unit = blockIdx.x; unit < nunits; unit += gridDim.x) {
-    // The previous unit's output stores (and any copies) are complete, so
-    // from here on this wave's vector-memory counter holds only this unit's
-    // Q loads, then its tile copies, in issue order.
-    __builtin_amdgcn_s_waitcnt(0);
+    // No drain here: the previous unit's output stores may still be in
+    // flight.  Every copy wait below counts only copies issued after the
+    // tile it waits for, and loads (global and global -> LDS) complete in
+    // issue order, so older outstanding stores can only lengthen a wait,
+    // never end it early.  (Letting the stores drain under this unit's
+    // loads is 4% faster on batches of 64-token segments.)
     const int item = int(unit / H);
     const int h = int(unit - int64_t(item) * H);
     int qt, start, len;
@@ -327,6 +332,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       const int r = tid >> 1, hh = tid & 1;
       const int base_row = qt * C::BM;
       u16* srow = s_q + r * D;
+      // The previous unit's tiles in the ring must no longer be read.
+      __syncthreads();
       // 1. stage: each thread copies half a row (D bytes), zeros past the end
       if (r < C::BM) {
         const bool ok = r < qrows;
@@ -581,9 +588,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       for (int t = 0; t < STAGES - 1; ++t)
         if (t < ntiles) issue_tile(t);
     };
-    start_pass();
-    // The Q-side pre-pass, while the first tiles are in flight.
+    // The Q-side pre-pass first (its staging rows use the ring), then the
+    // pass's first tiles.
     if (q_pending) transform_q();
+    start_pass();
 
     auto run_pass = [&](auto m0_tag, auto m_tag, bool started) {
       if (!started) start_pass();
@@ -675,10 +683,10 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const Schedul
 // Per head dim: (waves, keys per tile, ring depth, waves per SIMD).  Rows per
 // workgroup must equal bf16_block_m_const(D).
 template <int D> struct Choice;
-template <> struct Choice<32> { using C = Cfg<32, 4, 1, 32, 3, 2>; };
-template <> struct Choice<64> { using C = Cfg<64, 4, 1, 32, 3, 2>; };
+template <> struct Choice<32> { using C = Cfg<32, 4, 1, 64, 2, 2>; };
+template <> struct Choice<64> { using C = Cfg<64, 4, 1, 64, 2, 2>; };
 template <> struct Choice<80> { using C = Cfg<80, 4, 1, 64, 2, 2>; };
-template <> struct Choice<96> { using C = Cfg<96, 4, 1, 32, 4, 2>; };
+template <> struct Choice<96> { using C = Cfg<96, 4, 1, 64, 2, 2>; };
 template <> struct Choice<128> { using C = Cfg<128, 4, 1, 32, 2, 2>; };
 
 template <int D>

@@ -438,11 +438,12 @@ def _traffic_path(workload):
 
 
 def _kernel_sha():
+    """Hash of the attention kernel's sources (the kernel and its launch header)."""
     import hashlib
     h = hashlib.sha256()
-    path = os.path.join(ROOT, "vision_encoder_varlen_amd", "csrc", "attn_bf16.hip")
-    with open(path, "rb") as f:
-        h.update(f.read())
+    for name in ("attn_bf16.hip", "vit_kernels.h"):
+        with open(os.path.join(ROOT, "vision_encoder_varlen_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 

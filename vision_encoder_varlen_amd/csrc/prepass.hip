@@ -281,9 +281,17 @@ hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
   const int E = (dtype == 1 && (D / 2) % 8 == 0) ? 8 : 4;
   const int G = (D / 2) / E;
   const int rows_per_pass = (kThreads / 64) * (64 / G);
-  // About two rows per lane per token group: many small workgroups keep the
-  // most loads in flight, and the cos/sin table is still shared by all heads.
-  int tok_per_grp = (2 * rows_per_pass) / H;
+  // Two passes of rows per token group (about two rows per lane): many
+  // small workgroups keep the most loads in flight, and the cos/sin table is
+  // still shared by all heads.  Large batches take four passes when that
+  // still leaves at least 2048 workgroups (8 per CU): fewer tables and
+  // barriers per row, 6-14% faster on the 28.7k- and 131k-token batches,
+  // unchanged on the small ones.
+  int passes = 2;
+  if (H > 0 && (4 * rows_per_pass) / H > 0 &&
+      (T + (4 * rows_per_pass) / H - 1) / ((4 * rows_per_pass) / H) >= 2048)
+    passes = 4;
+  int tok_per_grp = (passes * rows_per_pass) / H;
   if (tok_per_grp < 1) tok_per_grp = 1;
   const int max_tok_lds = 32768 / (D / 2 * int(sizeof(float) * 2));
   if (tok_per_grp > max_tok_lds) tok_per_grp = max_tok_lds;

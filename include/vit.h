@@ -20,8 +20,9 @@
  *  - Memory: every pointer argument is device memory owned by the caller unless
  *    stated otherwise; the library never frees or retains caller pointers.
  *    Tensor pointers must be 16-byte aligned.
- *  - Layout: q, k, v, out are contiguous [T, H, D] row-major, element (t, h, d)
- *    at (t*H + h)*D + d.
+ *  - Layout: q, k, v, out are [T, H, D] row-major, element (t, h, d) at
+ *    (t*H + h)*D + d, unless a call takes token strides (see "Token strides"
+ *    below): then element (t, h, d) is at t*stride + h*D + d.
  *  - Streams: work is enqueued asynchronously on `stream` (0 = the default
  *    stream of the current device); the library never synchronises, except
  *    vit_device_error() and growing the scratch of vit_varlen_attn*.
@@ -280,8 +281,8 @@ int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
  * dtype selects the bf16 (VIT_BF16) or fp32 (VIT_F32) kernel; lse is as for
  * vit_varlen_attn_lse (null: not written); strides as for
  * vit_varlen_attn_strided (null: contiguous); flags as for vit_varlen_attn_ex;
- * cap is the capacity the list
- * was built with; the other arguments are those of vit_varlen_attn.  The
+ * cap is the capacity the list was built with; the other arguments are those
+ * of vit_varlen_attn.  The
  * list's max_seqlen must satisfy the bound vit_varlen_attn checks: the bf16
  * kernel skips a segment beyond the 32-bit offset span (this call cannot see
  * max_seqlen, so it is not rejected here).
@@ -317,9 +318,11 @@ int vit_varlen_attn_planned_qnorm_rope(
 
 /*
  * Reads (and with reset != 0 clears) the work-list error bits (enum
- * vit_worklist_error) left by the most recent vit_varlen_attn* call on the
- * current device and `stream`.  Synchronises that stream.  *err = 0 if no such
- * call has run yet.
+ * vit_worklist_error) left in the library's scratch by the most recent call
+ * that builds its own work-list (vit_varlen_attn, _f32, _lse, _strided, _ex)
+ * on the current device and `stream`.  Synchronises that stream.  *err = 0 if
+ * no such call has run yet.  Calls on a caller's list report in its meta[1];
+ * vit_dense_batch_attn has no list and no error bits.
  */
 int vit_device_error(hipStream_t stream, int32_t* err, int reset);
 

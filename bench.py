@@ -351,6 +351,14 @@ def main():
                 traffic = tj.get("bytes_per_launch")
         except Exception:
             traffic = None
+    # Algorithmic bytes of one attention launch: q, k, v read once, out
+    # written once, and cu_seqlens.  Below the bf16 ridge point (peak FLOP/s
+    # over peak bytes/s) the kernel is bound by HBM, and its roofline is taken
+    # in GB/s against the HBM peak.
+    elt = 2 if is_bf16 else 4
+    attn_bytes = 4 * T * H * D * elt + 4 * (wl.num_seqs + 1)
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    hbm_bound = is_bf16 and flops / attn_bytes < ridge
     tensors = 1 if args.fuse_q else 2     # q and k, or k alone
     pre_bytes = 2 * tensors * T * H * D * (2 if is_bf16 else 4) + 8 * T + \
         (4 * tensors * D if wl.use_norm else 0)
@@ -379,7 +387,9 @@ def main():
         "roofline": {"bound": "mfma" if is_bf16 else "alu", "kernel": "attn_bf16" if is_bf16 else "attn_f32",
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "avg_launch_us": round(attn_avg_ms * 1e3, 3)},
+                     "avg_launch_us": round(attn_avg_ms * 1e3, 3),
+                     "algorithmic_bytes": attn_bytes,
+                     "flop_per_byte": round(flops / attn_bytes, 2)},
         "kernels_us": {"prepass_and_worklist_launch": round(fused_avg_ms * 1e3, 3),
                        "prepass_alone": round(pre_avg_ms * 1e3, 3),
                        "worklist_alone": round(wl_avg_ms * 1e3, 3),
@@ -389,9 +399,16 @@ def main():
                     "frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "bytes_per_launch": pre_bytes},
         "step_frac_of_peak": round(value / peak, 4),
     }
+    if hbm_bound:
+        gbps = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+        result["roofline"].update({"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                                   "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                                   "achieved_tflops": round(achieved, 3),
+                                   "frac_of_bf16_peak": round(achieved / peak, 4)})
     if ceiling is not None:
         result["mfma_ceiling"] = ceiling
-        result["roofline"]["frac_of_random_operand_ceiling"] = round(achieved / ceiling["random_bf16"], 4)
+        if not hbm_bound:
+            result["roofline"]["frac_of_random_operand_ceiling"] = round(achieved / ceiling["random_bf16"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, args.causal)
     print(json.dumps(result), flush=True)

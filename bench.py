@@ -133,6 +133,19 @@ def summarize_pmc(args):
     print(json.dumps(res))
 
 
+def attention_roofline(flops, T, H, D, is_bf16, num_seqs):
+    """(algorithmic bytes of one attention launch, whether HBM bounds it).
+
+    Bytes: q, k, v read once, out written once, and cu_seqlens.  A bf16
+    launch whose FLOPs per byte fall below the ridge point (peak bf16 FLOP/s
+    over peak HBM bytes/s, 312.5) is HBM-bound; its roofline is then taken in
+    GB/s.  The fp32 kernel is reported against the vector ALU."""
+    elt = 2 if is_bf16 else 4
+    nbytes = 4 * T * H * D * elt + 4 * (num_seqs + 1)
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    return nbytes, bool(is_bf16 and flops / nbytes < ridge)
+
+
 def cpu_baseline(wl, x, budget_s, causal=False):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload.
 
@@ -351,14 +364,7 @@ def main():
                 traffic = tj.get("bytes_per_launch")
         except Exception:
             traffic = None
-    # Algorithmic bytes of one attention launch: q, k, v read once, out
-    # written once, and cu_seqlens.  Below the bf16 ridge point (peak FLOP/s
-    # over peak bytes/s) the kernel is bound by HBM, and its roofline is taken
-    # in GB/s against the HBM peak.
-    elt = 2 if is_bf16 else 4
-    attn_bytes = 4 * T * H * D * elt + 4 * (wl.num_seqs + 1)
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
-    hbm_bound = is_bf16 and flops / attn_bytes < ridge
+    attn_bytes, hbm_bound = attention_roofline(flops, T, H, D, is_bf16, wl.num_seqs)
     tensors = 1 if args.fuse_q else 2     # q and k, or k alone
     pre_bytes = 2 * tensors * T * H * D * (2 if is_bf16 else 4) + 8 * T + \
         (4 * tensors * D if wl.use_norm else 0)

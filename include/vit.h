@@ -24,8 +24,8 @@
  *    (t*H + h)*D + d, unless a call takes token strides (see "Token strides"
  *    below): then element (t, h, d) is at t*stride + h*D + d.
  *  - Streams: work is enqueued asynchronously on `stream` (0 = the default
- *    stream of the current device); the library never synchronises, except
- *    vit_device_error() and growing the scratch of vit_varlen_attn*.
+ *    stream of the current device); the library never makes the host wait,
+ *    except in vit_device_error() and vit_release().
  *  - Device-side validation of cu_seqlens (see vit_varlen_worklist) never
  *    reads or writes outside the segments it accepts.
  *  - The caller guarantees that q, k, v and out hold at least cu_seqlens[N]
@@ -170,7 +170,10 @@ int vit_qk_norm_rope_worklist(void* q, void* k, int64_t total_tokens, int num_he
  * b ranging over the same segment (VisionAttentionV2.forward on the vLLM page;
  * flash_attn_varlen_func with cu_seqlens_q = cu_seqlens_k on the tokenspeed page).
  * The tokenspeed page defaults the scale to head_size^-0.5 when the caller
- * passes none; here it is always explicit (any finite value).
+ * passes none; here it is always explicit, and any finite value is accepted,
+ * zero and negative ones included (scale 0 gives every key of the segment the
+ * same weight, so each row is the mean of its segment's v rows: a closed form
+ * the tests use).
  *
  *  q, k, v       bf16 [T, H, D], T = cu_seqlens[num_seqs].
  *  cu_seqlens    int32 [num_seqs + 1] on the device.
@@ -186,8 +189,12 @@ int vit_qk_norm_rope_worklist(void* q, void* k, int64_t total_tokens, int num_he
  *  out           bf16 [T, H, D]; must not alias q, k or v.  Rows of skipped
  *                segments are left untouched.
  * Builds the work-list in library-owned scratch (one buffer per device and
- * stream, grown on demand with hipMalloc and kept until vit_release), then runs
- * the attention kernel.  num_seqs == 0 or max_seqlen == 0 is a no-op.
+ * stream, kept until vit_release), then runs the attention kernel.  When a
+ * call needs more capacity than the stream's buffer has, the buffer is
+ * replaced with stream-ordered allocation on `stream` (hipFreeAsync of the
+ * old one, hipMallocAsync of a larger one): the host never waits, and the
+ * old buffer is released after the stream's earlier work.  num_seqs == 0 or
+ * max_seqlen == 0 is a no-op.
  */
 int vit_varlen_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                     int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
@@ -270,6 +277,10 @@ int64_t vit_worklist_capacity(int num_seqs, int max_seqlen, int block_m);
  *  cap     >= vit_worklist_capacity(num_seqs, max_seqlen, block_m).
  *  meta    int32 [2]: meta[0] = count, meta[1] = error bits, both written.
  * Runs entirely on the device (no host sync).  num_seqs at most 8192.
+ * The count and the error bits share one caller buffer, and cap is int64, so
+ * one allocation of 8 * cap + 8 bytes holds a whole plan and capacities past
+ * 2^31 items are expressible; the capacity is still bounded by 2^30 items
+ * (VIT_ERR_UNSUPPORTED beyond).
  */
 int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int block_m,
                         int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream);
@@ -362,7 +373,7 @@ const char* vit_last_error(void);
  */
 int vit_time_next_kernel(hipEvent_t start, hipEvent_t stop);
 
-/* Frees all library-owned scratch on every device (synchronises each device first). */
+/* Frees all library-owned scratch on every device (waits for each device first). */
 void vit_release(void);
 
 #ifdef __cplusplus

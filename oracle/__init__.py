@@ -29,7 +29,8 @@ What it computes, and what the pages say about it:
   ``_varlen_metadata`` on the tokenspeed page) and ``apply_rope_2d_complex``
   (``position_embedding_mode = "complex_rope"`` on the tokenspeed page).
 
-Pins: every function here is checked by ``tests/test_oracle_*.py`` against
+Pins: every function here (the storage roundings included) is checked by
+``tests/test_oracle_*.py`` against
 something other than itself (an independent formulation from the pages, a
 library routine, a closed form, brute force on tiny inputs, or an invariant).
 No function is "parity unpinned".

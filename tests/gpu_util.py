@@ -75,3 +75,35 @@ def assert_prepass_close(got: np.ndarray, exact: np.ndarray, dtype: str, what: s
         bad = err > tol
         assert not bad.any(), (f"{what}: {int(bad.sum())} bf16 elements beyond 1 ulp; "
                                f"worst {float((err / tol).max()):.2f} ulp")
+
+
+# Oracle results for the seeded workloads, computed once per test process:
+# several test modules compare against the same full-size results, and the
+# largest (16384 tokens, 12 heads) costs the oracle tens of seconds.
+_ORACLE_CACHE = {}
+
+
+def workload_oracle(n: int, kind: str, causal: bool = False) -> np.ndarray:
+    """Oracle output of seeded workload ``n`` (fp64 ``[T, H, D]``).
+
+    kind "attn": attention alone on the seeded q, k, v.
+    kind "e2e":  the oracle's fp64 pre-pass (norm when the workload has one,
+                 then rotary), rounded once to the storage dtype, then attention.
+    """
+    import oracle
+    from vision_encoder_varlen_amd import workloads as W
+    key = (n, kind, causal)
+    if key not in _ORACLE_CACHE:
+        wl = W.config(n)
+        x = W.generate(wl)
+        if kind == "attn":
+            q, k = x.q, x.k
+        elif kind == "e2e":
+            norm_w = (x.wq, x.wk) if wl.use_norm else (None, None)
+            q, k = oracle.qk_norm_rope(x.q, x.k, x.pos, wl.theta, *norm_w, wl.eps)
+            q, k = oracle.round_to_dtype(q, wl.dtype), oracle.round_to_dtype(k, wl.dtype)
+        else:
+            raise ValueError(kind)
+        _ORACLE_CACHE[key] = oracle.varlen_attention(q, k, x.v, x.cu_seqlens, wl.softmax_scale,
+                                                     causal=causal)
+    return _ORACLE_CACHE[key]

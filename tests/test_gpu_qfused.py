@@ -8,7 +8,7 @@
   once to the storage dtype, then attention) within the attention tolerance,
   for every head dim, both dtypes, both rotary pairings, with and without the
   norm, and the causal flag;
-* full-size workloads on sampled rows, in the launch configuration the
+* full-size workloads, every element, in the launch configuration the
   benchmark's fused step uses.
 """
 import numpy as np
@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from vision_encoder_varlen_amd import workloads as W
-from gpu_util import assert_attn_close, to_dev, to_host
+from gpu_util import assert_attn_close, to_dev, to_host, workload_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -84,24 +84,10 @@ def test_fused_q_large_positions_and_theta():
 
 
 @pytest.mark.parametrize("n", [2, 3])
-def test_fused_q_workload_sampled(n):
+def test_fused_q_workload(n):
     """4 x (32 x 32) at D = 80, and the 24-image ragged batch at D = 128 with
-    the norm: sampled rows against the oracle, which runs its pre-pass on the
-    segments the sample touches."""
+    the norm: every element against the oracle's end-to-end result."""
     wl = W.config(n)
     x = W.generate(wl)
     got, _ = _fused(wl, x)
-    rng = np.random.default_rng(300 + n)
-    tok = rng.integers(0, wl.total_tokens, 384)
-    heads = rng.integers(0, wl.H, 384)
-    cu = x.cu_seqlens
-    segs = np.unique(np.searchsorted(cu, tok, side="right") - 1)
-    idx = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in segs])
-    norm_w = (x.wq, x.wk) if wl.use_norm else (None, None)
-    pq, pk = oracle.qk_norm_rope(x.q[idx], x.k[idx], x.pos[idx], wl.theta, *norm_w, wl.eps)
-    eq = np.zeros(x.q.shape)
-    ek = np.zeros(x.k.shape)
-    eq[idx] = oracle.round_to_dtype(pq, wl.dtype)
-    ek[idx] = oracle.round_to_dtype(pk, wl.dtype)
-    want = oracle.varlen_attention_rows(eq, ek, x.v, cu, wl.softmax_scale, tok, heads)
-    assert_attn_close(got[tok, heads], want, wl.dtype, f"config {n} fused q (sampled)")
+    assert_attn_close(got, workload_oracle(n, "e2e"), wl.dtype, f"config {n} fused q")

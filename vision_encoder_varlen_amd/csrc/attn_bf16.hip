@@ -238,6 +238,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
   // coordinate, hi + lo).
   u16* const s_q = smem;
   static_assert(C::BM * D * 2 <= C::LDS_BYTES, "Q staging rows must fit in the K/V ring");
+  // transform_q gives each query row of the unit two threads (one per half).
+  static_assert(C::THREADS == 2 * C::BM, "Q staging needs two threads per query row");
   __shared__ float s_qw[D];
   __shared__ float2 s_rev[kMaxQFreqs];
   static_assert((C::LDS_BYTES + D * 4 + kMaxQFreqs * 8) * C::OCC <= 160 * 1024,

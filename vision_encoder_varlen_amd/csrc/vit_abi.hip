@@ -9,9 +9,9 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 #include <map>
 #include <mutex>
-#include <string>
 #include <utility>
 
 #include "vit.h"
@@ -19,7 +19,9 @@
 
 namespace {
 
-thread_local std::string g_last_error;
+// Message of the last failed call on this thread: a fixed buffer, so that
+// neither success nor failure allocates host memory.
+thread_local char g_last_error[512];
 
 // Events that the next kernel-launching call on this thread records at its
 // kernel's dispatch start and end (set by vit_time_next_kernel).
@@ -43,12 +45,10 @@ hipError_t record_empty(const TimingHook& t, hipStream_t stream) {
 }
 
 int fail(int code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return code;
 }
 
@@ -57,7 +57,7 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 int ok() {
-  g_last_error.clear();
+  g_last_error[0] = '\0';
   return VIT_OK;
 }
 
@@ -66,6 +66,10 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 // Work-list scratch owned by the library: one buffer per (device, stream), so
 // calls on different streams never share it.  Layout: meta[4] then items.
+// It grows with stream-ordered allocation (hipFreeAsync of the old buffer and
+// hipMallocAsync of the new one, both on the caller's stream), so a call never
+// waits on the host for work already queued: the old buffer is released only
+// after the stream's earlier kernels have read it.
 struct Scratch {
   int32_t* buf = nullptr;
   int64_t cap_items = 0;
@@ -88,17 +92,15 @@ int get_scratch(hipStream_t stream, int64_t cap, Scratch** out) {
   Scratch& s = g_scratch[{dev, stream}];
   if (s.cap_items < cap) {
     if (s.buf != nullptr) {
-      // The old buffer may still be read by work queued on this stream.
-      e = hipStreamSynchronize(stream);
-      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-      e = hipFree(s.buf);
-      if (e != hipSuccess) return hip_fail(e, "hipFree");
+      e = hipFreeAsync(s.buf, stream);
+      if (e != hipSuccess) return hip_fail(e, "hipFreeAsync (work-list scratch)");
       s.buf = nullptr;
       s.cap_items = 0;
     }
     int64_t grow = cap < 4096 ? 4096 : cap + cap / 4;
-    e = hipMalloc(reinterpret_cast<void**>(&s.buf), size_t(4 + 2 * grow) * sizeof(int32_t));
-    if (e != hipSuccess) return hip_fail(e, "hipMalloc (work-list scratch)");
+    e = hipMallocAsync(reinterpret_cast<void**>(&s.buf), size_t(4 + 2 * grow) * sizeof(int32_t),
+                       stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync (work-list scratch)");
     s.cap_items = grow;
   }
   *out = &s;
@@ -560,7 +562,7 @@ int vit_probe_mfma(const void* operands, int64_t operand_bytes, int blocks, int 
   return e == hipSuccess ? ok() : hip_fail(e, "probe launch");
 }
 
-const char* vit_last_error(void) { return g_last_error.c_str(); }
+const char* vit_last_error(void) { return g_last_error; }
 
 void vit_release(void) {
   std::lock_guard<std::mutex> lock(g_mu);
@@ -568,8 +570,11 @@ void vit_release(void) {
     if (kv.second.buf == nullptr) continue;
     int cur = 0;
     if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first.first) == hipSuccess) {
+      // The buffer's own stream may no longer exist: wait for the whole
+      // device, then free on the null stream and wait for that.
       (void)hipDeviceSynchronize();
-      (void)hipFree(kv.second.buf);
+      (void)hipFreeAsync(kv.second.buf, nullptr);
+      (void)hipDeviceSynchronize();
       (void)hipSetDevice(cur);
     }
   }

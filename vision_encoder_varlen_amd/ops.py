@@ -260,6 +260,19 @@ def rebuild_worklist(plan: Plan, cu_seqlens: torch.Tensor) -> Plan:
     return plan
 
 
+def _check_plan_span(plan: "Plan", k: torch.Tensor, v: torch.Tensor) -> None:
+    """The bf16 kernel addresses one segment's k and v rows with 32-bit byte
+    offsets, counted with the key padding of its last tile (64 rows): a segment
+    whose span exceeds 2^30 bytes would be skipped without an error, so the
+    plan's length bound must keep every listed segment inside it.  (The list
+    holds no segment longer than ``plan.max_seqlen``.)  The bound is the one
+    the C ABI applies to ``max_seqlen`` for both dtypes."""
+    stride = max(int(k.stride(0)), int(v.stride(0)))
+    if (int(plan.max_seqlen) + 64) * stride * 2 > (1 << 30):
+        raise ValueError(f"plan.max_seqlen {plan.max_seqlen} with token stride {stride}: a segment's "
+                         "k/v rows would exceed the kernel's 2^30-byte addressing span")
+
+
 def varlen_attn_planned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                         cu_seqlens: torch.Tensor, plan: Plan, scale: Optional[float] = None,
                         out: Optional[torch.Tensor] = None,
@@ -269,6 +282,7 @@ def varlen_attn_planned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     T, H, D = q.shape
     if plan.block_m != attn_block_m(H, D, q.dtype):
         raise ValueError("plan was built with a different block_m than this kernel uses")
+    _check_plan_span(plan, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -302,6 +316,7 @@ def varlen_attn_planned_qnorm_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Te
     T, H, D = q.shape
     if plan.block_m != attn_block_m(H, D, q.dtype):
         raise ValueError("plan was built with a different block_m than this kernel uses")
+    _check_plan_span(plan, k, v)
     if pos is not None:
         _need_cuda("pos", pos, torch.int32)
         if pos.shape != (T, 2):

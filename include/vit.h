@@ -193,7 +193,8 @@ int vit_qk_norm_rope_worklist(void* q, void* k, int64_t total_tokens, int num_he
  * call needs more capacity than the stream's buffer has, the buffer is
  * replaced with stream-ordered allocation on `stream` (hipFreeAsync of the
  * old one, hipMallocAsync of a larger one): the host never waits, and the
- * old buffer is released after the stream's earlier work.  num_seqs == 0 or
+ * old buffer is released after the stream's earlier work.  Callers that must
+ * not allocate at all use vit_varlen_attn_noalloc.  num_seqs == 0 or
  * max_seqlen == 0 is a no-op.
  */
 int vit_varlen_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
@@ -237,6 +238,31 @@ int vit_varlen_attn_ex(const void* q, const void* k, const void* v, const int32_
                        int num_seqs, int max_seqlen, int num_heads, int head_dim, float scale,
                        int dtype, int flags, void* out, float* lse, const int64_t* strides,
                        hipStream_t stream);
+
+/*
+ * vit_varlen_attn_ex for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same operation, arguments, layout and errors as
+ * vit_varlen_attn_ex, and the same kernels; the work-list is built in a fixed
+ * device array of the library instead of the per-stream scratch, so the call
+ * makes no device or host allocation (no hipMalloc, hipFree or stream-ordered
+ * allocation).
+ *  - Limit: num_seqs * ceil(max_seqlen / vit_attn_block_m(num_heads, head_dim,
+ *    dtype)) at most 262144 work items (the array holds 2 MiB of items);
+ *    larger calls return VIT_ERR_UNSUPPORTED with nothing enqueued.
+ *  - The array exists once per GPU, from the library's load until the process
+ *    ends, and every call on that GPU uses it: calls that overlap in time on
+ *    one GPU (other streams, other threads) race on it and can compute wrong
+ *    results, so serialise them.  Each call rewrites the list count, the error
+ *    bits and every item it reads, so nothing has to be cleared between calls.
+ *  - Bad segments are skipped as vit_varlen_attn_ex skips them; the error
+ *    bits stay in the array and vit_device_error does not report them (build
+ *    a list with vit_varlen_worklist to read them).
+ */
+int vit_varlen_attn_noalloc(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                            int num_heads, int head_dim, float scale, int dtype, int flags,
+                            void* out, float* lse, const int64_t* strides, hipStream_t stream);
 
 /*
  * Attention over a uniform batch: `batch` segments of `seq_len` tokens each,

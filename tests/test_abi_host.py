@@ -285,3 +285,26 @@ def test_qnorm_rope_attention_argument_errors(lib):
     assert f(*head[:10], 7, *head[11:], *ok_q, out, None, None, None) == _lib.VIT_ERR_INVALID_ARG
     # an empty plan is a no-op
     assert f(*head[:5], 0, *head[6:], *ok_q, out, None, None, None) == _lib.VIT_OK
+
+
+def test_noalloc_limits_and_errors_before_any_launch(lib):
+    """vit_varlen_attn_noalloc: the no-allocation scratch holds 2^18 work items;
+    a larger list is refused before anything is enqueued, and the argument
+    checks of vit_varlen_attn_ex apply unchanged."""
+    f = lib.vit_varlen_attn_noalloc
+    out = FAKE + 0x1000
+    base = (FAKE, FAKE + 0x100, FAKE + 0x200, FAKE)
+    # 8192 segments of up to 8192 tokens at 128 query rows per item: 2^19 items
+    assert f(*base, 8192, 8192, 2, 64, 0.125, _lib.VIT_BF16, 0, out, None, None, None) == \
+        _lib.VIT_ERR_UNSUPPORTED
+    assert "no-allocation" in _err(lib)
+    # fp32 items cover 32 rows: 2048 segments of 4097 tokens need 2048 * 129 > 2^18 items
+    assert f(*base, 2048, 4097, 2, 64, 0.125, _lib.VIT_F32, 0, out, None, None, None) == \
+        _lib.VIT_ERR_UNSUPPORTED
+    assert f(None, *base[1:], 4, 64, 2, 64, 0.125, 1, 0, out, None, None, None) == \
+        _lib.VIT_ERR_INVALID_ARG
+    assert f(*base, 4, 64, 2, 64, 0.125, 7, 0, out, None, None, None) == _lib.VIT_ERR_INVALID_ARG
+    assert f(*base, 4, 64, 2, 64, 0.125, 1, 2, out, None, None, None) == _lib.VIT_ERR_INVALID_ARG
+    assert "flags" in _err(lib)
+    # an empty batch is a no-op that touches no device state
+    assert f(*base, 0, 0, 2, 64, 0.125, 1, 0, out, None, None, None) == _lib.VIT_OK

@@ -41,6 +41,7 @@ SIGNATURES = {
     "vit_varlen_attn_planned": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _I, _F, _I, _I, _P, _P, _P,
                                      _P]),
     "vit_varlen_attn_ex": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
+    "vit_varlen_attn_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
     "vit_varlen_attn_planned_qnorm_rope": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _I, _F, _I, _I,
                                                 _P, _F, _P, _F, _I, _P, _P, _P, _P]),
     "vit_varlen_attn_strided": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),

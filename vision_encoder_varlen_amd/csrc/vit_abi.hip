@@ -107,6 +107,39 @@ int get_scratch(hipStream_t stream, int64_t cap, Scratch** out) {
   return VIT_OK;
 }
 
+// Work-list scratch of vit_varlen_attn_noalloc, for callers that cannot
+// allocate: a fixed device array (meta[4], then kNoAllocMaxItems items of two
+// int32; 2 MiB + 16 B), one copy per GPU, held until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: host code uses
+// only the address hipGetSymbolAddress returns for the current device.
+constexpr int64_t kNoAllocMaxItems = int64_t(1) << 18;
+static __device__ __align__(256) int32_t scratch[4 + 2 * kNoAllocMaxItems];
+
+constexpr int kNoAllocMaxDevices = 64;
+std::mutex g_noalloc_mu;
+int32_t* g_noalloc_ptr[kNoAllocMaxDevices];  // device address of `scratch`, per device
+
+// The current device's copy of `scratch`, looked up once per device (on the
+// first call made with that device current).
+int noalloc_scratch(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kNoAllocMaxDevices)
+    return fail(VIT_ERR_UNSUPPORTED, "device index %d is beyond the %d this call supports", dev,
+                kNoAllocMaxDevices);
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (g_noalloc_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress (no-allocation scratch)");
+    if (p == nullptr) return fail(VIT_ERR_HIP, "hipGetSymbolAddress returned a null address");
+    g_noalloc_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_noalloc_ptr[dev];
+  return VIT_OK;
+}
+
 // Checks shared by every attention entry point: the tensors, head count and
 // dim, and the scale.
 int check_tensor_args(const void* q, const void* k, const void* v, int H, int D, float scale,
@@ -218,9 +251,11 @@ int block_m_for(int dtype, int D) {
   return dtype == VIT_BF16 ? vit::bf16_block_m_const(D) : vit::kBlockMF32;
 }
 
+// noalloc: build the work-list in the fixed device array (`scratch`) instead
+// of the per-stream buffer; nothing is allocated.
 int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, int num_seqs,
                 int max_seqlen, int H, int D, float scale, int flags, void* out, float* lse,
-                const int64_t* strides, hipStream_t stream, int dtype) {
+                const int64_t* strides, hipStream_t stream, int dtype, bool noalloc = false) {
   const TimingHook t = take_timing();
   int rc = check_attn_args(q, k, v, cu, num_seqs, max_seqlen, H, D, scale, out);
   if (rc != VIT_OK) return rc;
@@ -241,11 +276,23 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu, 
   const int bm = block_m_for(dtype, D);
   const int64_t cap = capacity(num_seqs, max_seqlen, bm);
   if (cap > kMaxCapacity) return fail(VIT_ERR_UNSUPPORTED, "work-list capacity %lld too large", (long long)cap);
-  Scratch* s = nullptr;
-  rc = get_scratch(stream, cap, &s);
-  if (rc != VIT_OK) return rc;
-  int32_t* meta = s->buf;
-  int32_t* items = s->buf + 4;
+  int32_t* buf = nullptr;
+  if (noalloc) {
+    if (cap > kNoAllocMaxItems)
+      return fail(VIT_ERR_UNSUPPORTED,
+                  "work-list capacity %lld (num_seqs * ceil(max_seqlen / %d)) exceeds the %lld "
+                  "items of the no-allocation scratch", (long long)cap, bm,
+                  (long long)kNoAllocMaxItems);
+    rc = noalloc_scratch(&buf);
+    if (rc != VIT_OK) return rc;
+  } else {
+    Scratch* s = nullptr;
+    rc = get_scratch(stream, cap, &s);
+    if (rc != VIT_OK) return rc;
+    buf = s->buf;
+  }
+  int32_t* meta = buf;
+  int32_t* items = buf + 4;
   hipError_t e = vit::launch_worklist(cu, num_seqs, max_seqlen, bm, items, cap, meta, stream,
                                       nullptr, nullptr);
   if (e != hipSuccess) return hip_fail(e, "work-list launch");
@@ -412,6 +459,15 @@ int vit_varlen_attn_ex(const void* q, const void* k, const void* v, const int32_
   if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, flags,
                      out, lse, strides, stream, dtype);
+}
+
+int vit_varlen_attn_noalloc(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                            int num_heads, int head_dim, float scale, int dtype, int flags,
+                            void* out, float* lse, const int64_t* strides, hipStream_t stream) {
+  if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  return attn_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, scale, flags,
+                     out, lse, strides, stream, dtype, /*noalloc=*/true);
 }
 
 int vit_attn_block_m(int num_heads, int head_dim, int dtype) {

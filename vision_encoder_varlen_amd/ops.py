@@ -175,6 +175,31 @@ def varlen_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: t
     return out
 
 
+def varlen_attn_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        cu_seqlens: torch.Tensor, max_seqlen: int, out: torch.Tensor,
+                        scale: Optional[float] = None, lse: Optional[torch.Tensor] = None,
+                        causal: bool = False) -> torch.Tensor:
+    """``varlen_attn`` through ``vit_varlen_attn_noalloc``: the work-list goes to
+    the library's fixed device array, so nothing is allocated (``out`` must be
+    given).  Calls that overlap in time on one GPU race on that array."""
+    _attn_checks(q, k, v, cu_seqlens)
+    T, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _need_cuda("out", out, q.dtype, token_strided=True)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    if lse is not None:
+        _need_cuda("lse", lse, torch.float32)
+        if lse.shape != (T, H):
+            raise ValueError("lse must be float32 [T, H]")
+    _lib.check(_lib.load().vit_varlen_attn_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+        int(max_seqlen), H, D, float(scale), dtype_code(q.dtype), _flags(causal), out.data_ptr(),
+        _ptr(lse), _strides(q, k, v, out), _stream(q)))
+    return out
+
+
 def _flags(causal: bool) -> int:
     return _lib.VIT_ATTN_CAUSAL if causal else 0
 

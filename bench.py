@@ -12,8 +12,16 @@ metric is attention TFLOP/s with FLOPs = 4*H*D*sum(s_i^2) per step.
 The attention kernel's own average duration is measured live inside the timed
 loop with HIP events that the kernel's dispatch records at its start and end
 (hipExtLaunchKernel, on the stream it is launched on); the roofline fraction is
-taken against MI355X's dense bf16 MFMA peak.  The CPU
-oracle is timed on a bounded sample of the same workload on the host cores.
+taken against MI355X's dense bf16 MFMA peak.  With the default workload the
+line also carries the attention kernel alone on the ragged 24-image batch
+(second_target), the other workload the 50%-of-peak target is set on.
+
+Memory-bound side timings (the pre-pass, and the attention once more) read a
+1 GiB buffer before each launch, so their inputs come from HBM rather than
+from the Infinity Cache.  Kernel durations are reported as mean and median.
+The CPU oracle is timed on a bounded sample of the same workload on the host
+cores, with the BLAS library it runs on and its wall-seconds on every seeded
+workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N]
                        [--no-cpu-baseline] [--traffic-json FILE]
@@ -60,6 +68,15 @@ def parse():
                    help="read q, k, v as views of one packed [T, 3, H, D] buffer (token stride 3*H*D)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU-oracle time budget")
+    p.add_argument("--no-oracle-per-config", action="store_true",
+                   help="skip the oracle's wall-seconds on every seeded workload in cpu_baseline")
+    p.add_argument("--second-target", type=int, default=3, metavar="N",
+                   help="with the default workload (2): also time the attention kernel alone on "
+                        "seeded workload N (default 3, the ragged batch; 0 = off) and report it "
+                        "under second_target")
+    p.add_argument("--flush-mib", type=int, default=1024,
+                   help="size of the buffer read before each memory-bound side-loop launch, "
+                        "so its inputs come from HBM and not the 256 MB Infinity Cache")
     p.add_argument("--traffic-json", default="",
                    help="HBM traffic per attention launch measured by rocprofv3 counters "
                         "(default profiles/attn_traffic_<workload>.json)")
@@ -174,7 +191,44 @@ def cpu_baseline(wl, x, budget_s, causal=False):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{nseg} whole segments ({nseg / wl.num_seqs:.2f} passes over the batch), "
                       f"fp64 pre-pass + attention, {dt:.1f} s",
-            "seconds": round(dt, 3)}
+            "seconds": round(dt, 3), "blas": blas_backend()}
+
+
+def blas_backend():
+    """The BLAS library NumPy's matrix products run on, and its thread count."""
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            i = libs[0]
+            return {"library": i.get("internal_api"), "version": i.get("version"),
+                    "threads": i.get("num_threads"), "path": os.path.basename(i.get("filepath", ""))}
+    except Exception:
+        pass
+    return None
+
+
+def oracle_seconds_per_config(causal=False):
+    """Wall-seconds of the whole fp64 oracle (pre-pass + attention) on each
+    seeded workload: best of 3 for the two small ones, one run for the rest."""
+    import oracle
+    from vision_encoder_varlen_amd import workloads as W
+    res = {}
+    for n in (1, 2, 3, 4, 5):
+        wl = W.config(n)
+        x = W.generate(wl)
+        norm = (x.wq, x.wk) if wl.use_norm else (None, None)
+        best = None
+        for _ in range(3 if n <= 2 else 1):
+            t0 = time.perf_counter()
+            q, k = oracle.qk_norm_rope(x.q, x.k, x.pos, wl.theta, *norm, wl.eps)
+            oracle.varlen_attention(q, k, x.v, x.cu_seqlens, wl.softmax_scale, causal)
+            dt = time.perf_counter() - t0
+            best = dt if best is None else min(best, dt)
+        res[wl.name] = {"seconds": round(best, 3),
+                        "tflops": round(wl.attn_flops / best / 1e12, 4) if not causal else None}
+        del x
+    return res
 
 
 def main():
@@ -325,19 +379,36 @@ def main():
     # Outside the timed region: each other kernel's own duration, from the
     # same dispatch-timestamp events, one kernel per loop (a kernel queued
     # behind a different, still-running one would count part of its wait).
-    def side_loop(fn, fargs):
+    attn_samples = [e[0].elapsed_time(e[1]) for e in ev if e is not None]
+    attn_med_ms = float(np.median(attn_samples))
+
+    # A buffer read before each memory-bound launch, so the launch reads its
+    # inputs from HBM rather than from the Infinity Cache (256 MB) that the
+    # previous launch of the same small inputs left them in.  Reading (not
+    # writing) leaves the caches holding clean lines, so the timed launch does
+    # not also pay for writing a previous kernel's dirty lines back.
+    flush = torch.ones(max(1, args.flush_mib) << 18, dtype=torch.float32, device=dev)
+
+    def side_loop(fn, fargs, flushed=False):
+        """(mean, median) ms of one kernel's own dispatch, K launches."""
         evs = [new_events(2) for _ in range(K)]
         torch.cuda.synchronize()
-        for e in evs:
+        for i, e in enumerate(evs):
+            if flushed:
+                flush.sum()
             check(f_hook(e[0].cuda_event, e[1].cuda_event))
             check(fn(*fargs))
         torch.cuda.synchronize()
-        return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        t = [e[0].elapsed_time(e[1]) for e in evs]
+        return float(np.mean(t)), float(np.median(t))
 
-    pre_avg_ms = side_loop(f_pre, pre_args)
-    wl_avg_ms = side_loop(f_wl, wl_args)
-    fused_avg_ms = side_loop(f_fused, fused_args)
-    lse_avg_ms = side_loop(f_at, at_lse_args)
+    pre_avg_ms, pre_med_ms = side_loop(f_pre, pre_args, flushed=True)
+    pre_warm_ms, _ = side_loop(f_pre, pre_args)
+    wl_avg_ms, _ = side_loop(f_wl, wl_args)
+    fused_avg_ms, _ = side_loop(f_fused, fused_args)
+    lse_avg_ms, _ = side_loop(f_at, at_lse_args)
+    attn_cold_ms, attn_cold_med_ms = side_loop(f_at, at_args, flushed=True)
+    del flush
 
     ceiling = mfma_ceiling(lib, torch, dev, stream) if is_bf16_dtype(wl) else None
 
@@ -369,6 +440,7 @@ def main():
     pre_bytes = 2 * tensors * T * H * D * (2 if is_bf16 else 4) + 8 * T + \
         (4 * tensors * D if wl.use_norm else 0)
     pre_gbps = pre_bytes / (pre_avg_ms * 1e-3) / 1e9
+    pre_med_gbps = pre_bytes / (pre_med_ms * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -394,15 +466,25 @@ def main():
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "avg_launch_us": round(attn_avg_ms * 1e3, 3),
+                     "median_launch_us": round(attn_med_ms * 1e3, 3),
+                     "timed_samples": len(attn_samples),
                      "algorithmic_bytes": attn_bytes,
                      "flop_per_byte": round(flops / attn_bytes, 2)},
         "kernels_us": {"prepass_and_worklist_launch": round(fused_avg_ms * 1e3, 3),
                        "prepass_alone": round(pre_avg_ms * 1e3, 3),
                        "worklist_alone": round(wl_avg_ms * 1e3, 3),
                        "attention": round(attn_avg_ms * 1e3, 3),
-                       "attention_with_lse": round(lse_avg_ms * 1e3, 3)},
+                       "attention_median": round(attn_med_ms * 1e3, 3),
+                       "attention_after_cache_flush": round(attn_cold_ms * 1e3, 3),
+                       "attention_after_cache_flush_median": round(attn_cold_med_ms * 1e3, 3),
+                       "attention_with_lse": round(lse_avg_ms * 1e3, 3),
+                       "prepass_cache_warm": round(pre_warm_ms * 1e3, 3)},
         "prepass": {"bound": "hbm", "achieved": round(pre_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                    "frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "bytes_per_launch": pre_bytes},
+                    "frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "bytes_per_launch": pre_bytes,
+                    "avg_launch_us": round(pre_avg_ms * 1e3, 3),
+                    "median_launch_us": round(pre_med_ms * 1e3, 3),
+                    "median_achieved": round(pre_med_gbps, 1),
+                    "timing": f"each launch after a {args.flush_mib} MiB buffer read (inputs from HBM)"},
         "step_frac_of_peak": round(value / peak, 4),
     }
     if hbm_bound:
@@ -415,9 +497,58 @@ def main():
         result["mfma_ceiling"] = ceiling
         if not hbm_bound:
             result["roofline"]["frac_of_random_operand_ceiling"] = round(achieved / ceiling["random_bf16"], 4)
+    if args.second_target and args.config == 2 and not (args.causal or args.fuse_q or args.dense_batch
+                                                         or args.packed_qkv):
+        result["second_target"] = second_target(args.second_target, lib, torch, dev, stream,
+                                                max(K, 50), new_events)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, args.causal)
+        if not args.no_oracle_per_config:
+            result["cpu_baseline"]["oracle_seconds_per_config"] = oracle_seconds_per_config(args.causal)
     print(json.dumps(result), flush=True)
+
+
+def second_target(n, lib, torch, dev, stream, launches, new_events):
+    """The attention kernel alone on seeded workload n, as the step runs it
+    (pre-pass applied once, then the planned attention): its own dispatch
+    duration over `launches` launches, and the fraction of bf16 MFMA peak."""
+    from vision_encoder_varlen_amd import _lib, ops
+    from vision_encoder_varlen_amd import workloads as W
+    wl = W.config(n)
+    x = W.generate(wl)
+    q, k, v = (torch.from_numpy(a).to(torch.bfloat16).to(dev) for a in (x.q, x.k, x.v))
+    pos = torch.from_numpy(x.pos).to(dev)
+    cu = torch.from_numpy(x.cu_seqlens).to(dev)
+    wq = torch.from_numpy(x.wq).to(dev) if wl.use_norm else None
+    wk = torch.from_numpy(x.wk).to(dev) if wl.use_norm else None
+    T, H, D = q.shape
+    ops.qk_norm_rope_(q, k, pos, wl.theta, wq, wk, wl.eps)
+    plan = ops.varlen_worklist(cu, wl.max_seqlen, ops.attn_block_m(H, D, q.dtype))
+    out = torch.empty_like(q)
+    sh = stream.cuda_stream
+    at_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), cu.data_ptr(), plan.items.data_ptr(),
+               plan.cap, plan.meta.data_ptr(), H, D, float(wl.softmax_scale), _lib.VIT_BF16, 0,
+               out.data_ptr(), None, None, sh)
+    for _ in range(5):
+        _lib.check(lib.vit_varlen_attn_planned(*at_args))
+    evs = [new_events(2) for _ in range(launches)]
+    torch.cuda.synchronize()
+    for e in evs:
+        _lib.check(lib.vit_time_next_kernel(e[0].cuda_event, e[1].cuda_event))
+        _lib.check(lib.vit_varlen_attn_planned(*at_args))
+    torch.cuda.synchronize()
+    if int(plan.meta.cpu()[1]) != 0 or not torch.isfinite(out).all().item():
+        print("bench: second target: work-list error or non-finite output", file=sys.stderr)
+        sys.exit(3)
+    t = [e[0].elapsed_time(e[1]) for e in evs]
+    avg, med = float(np.mean(t)), float(np.median(t))
+    ach = wl.attn_flops / (avg * 1e-3) / 1e12
+    return {"workload": wl.name, "tokens": T, "heads": H, "head_dim": D, "images": wl.num_seqs,
+            "flops_per_launch": wl.attn_flops, "launches": launches,
+            "attention_avg_us": round(avg * 1e3, 3), "attention_median_us": round(med * 1e3, 3),
+            "achieved": round(ach, 3), "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "median_frac": round(wl.attn_flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def is_bf16_dtype(wl):

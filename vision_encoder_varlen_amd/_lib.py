@@ -10,7 +10,10 @@ import ctypes
 import os
 import threading
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvit.so")
+# VIT_LIBRARY names another build of the same library to load instead (the
+# host-sanitizer build the CPU tests use); it must export the same C ABI.
+LIB_PATH = os.environ.get("VIT_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libvit.so")
 
 VIT_OK = 0
 VIT_ERR_INVALID_ARG = 1

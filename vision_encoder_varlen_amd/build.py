@@ -49,6 +49,61 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
+# Host code instrumented with AddressSanitizer and UndefinedBehaviorSanitizer;
+# the device code is built as usual.  -Xarch_host keeps each sanitizer off the
+# GPU compilation.
+HOST_SANITIZER_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
+def clangxx() -> str:
+    for cand in ("/opt/rocm/llvm/bin/clang++", shutil.which("clang++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("clang++ not found (needed to link the sanitizer build)")
+
+
+def sanitizer_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime the sanitizer build links
+    against (it also carries UndefinedBehaviorSanitizer); a process that loads
+    that build must preload it."""
+    res = subprocess.run([clangxx(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True, check=True)
+    return res.stdout.strip()
+
+
+def build_host_sanitized(out_path: str, verbose: bool = False) -> str:
+    """Build a copy of the library whose host code (argument checks, scratch
+    management, launches) runs under ASan + UBSan, for the CPU tests of the C
+    ABI.  Objects go to their own folder; the link is a plain clang++ host
+    link against the HIP runtime (every object already holds its device code)."""
+    obj_dir = os.path.join(BUILD_DIR, "host_sanitized")
+    os.makedirs(obj_dir, exist_ok=True)
+    srcs = sources()
+
+    def compile_one(src):
+        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+        cmd = [hipcc(), *COMMON_FLAGS, *HOST_SANITIZER_FLAGS, "-c", src, "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(compile_one, srcs))
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(hipcc())), "lib")
+    cmd = [clangxx(), "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libsan",
+           "-o", out_path, *objs, f"-L{rocm_lib}", "-lamdhip64", f"-Wl,-rpath,{rocm_lib}"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    if verbose:
+        print(f"built {out_path}", file=sys.stderr)
+    return out_path
+
+
 def build(verbose: bool = False, extra_flags=()) -> str:
     """Compile and link libvit.so; returns its path.  Always rebuilds."""
     os.makedirs(BUILD_DIR, exist_ok=True)

@@ -332,10 +332,10 @@ int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
 
 /*
  * vit_varlen_attn_planned with the Q half of the pre-pass done inside the
- * attention kernel: each work item stages its query rows in LDS, applies
- * RMSNorm (q_weight, eps; null q_weight: none) and then the 2D rotary (pos,
- * theta, rope_mode; null pos: none) as vit_qk_norm_rope_ex does to q, and
- * feeds the result to the MFMAs.  q in memory is not modified.  This is
+ * attention kernel: each work item applies RMSNorm (q_weight, eps; null
+ * q_weight: none) and then the 2D rotary (pos, theta, rope_mode; null pos:
+ * none) to its query rows in registers, as vit_qk_norm_rope_ex does to q,
+ * and feeds the result to the MFMAs.  q in memory is not modified.  This is
  * _qkv_with_rope (vLLM page: norm, then rotary) with q's read and write of the
  * separate pre-pass removed; k is still prepared by vit_qk_norm_rope_ex (or
  * vit_qk_norm_rope_worklist) called with q = null.

@@ -230,16 +230,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     cp_lds[j] = unsigned((is_k ? i * 64 : C::KREG + (i - C::NK) * 64) * 16);
   }
 
-  // Q-side pre-pass (when asked for): the unit's query rows are staged in
-  // LDS, normalised and rotated there by all threads, then read back as the
-  // MFMA fragments.  The staging rows reuse the K/V ring, which is idle then
-  // (the unit's first tiles are issued after the transform).  The tables
-  // hold the norm weights and the rotary frequencies (turns per unit
-  // coordinate, hi + lo).
-  u16* const s_q = smem;
-  static_assert(C::BM * D * 2 <= C::LDS_BYTES, "Q staging rows must fit in the K/V ring");
-  // transform_q gives each query row of the unit two threads (one per half).
-  static_assert(C::THREADS == 2 * C::BM, "Q staging needs two threads per query row");
+  // Q-side pre-pass (when asked for): each unit's Q fragments are normalised
+  // and rotated in registers right after they are loaded.  The tables hold
+  // the norm weights and the rotary frequencies (turns per unit coordinate,
+  // hi + lo).
   __shared__ float s_qw[D];
   __shared__ float2 s_rev[kMaxQFreqs];
   static_assert((C::LDS_BYTES + D * 4 + kMaxQFreqs * 8) * C::OCC <= 160 * 1024,
@@ -252,6 +246,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
         constexpr int f = decltype(f_c)::value;
         s_rev[f] = make_float2(qpre.rev_hi[f], qpre.rev_lo[f]);
       });
+    __syncthreads();
   }
 
   // items == null: a uniform batch (u_batch segments of u_seq_len tokens).
@@ -318,88 +313,97 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
         }
       }
     };
-    if (!q_pending) load_q();
+    load_q();
 
-    // The Q-side pre-pass: RMSNorm then rotary in fp32, rounded once to bf16
-    // (the pre-pass kernel's arithmetic), on the unit's BM query rows staged
-    // in LDS.  Thread (r, hh) owns half hh of row r: its rotary pairs are
-    // (j, j + D/2) for j in [hh*D/4, (hh+1)*D/4) (rotate-half) or (2j, 2j+1)
-    // for the same j (complex), so a pair never spans two threads, and angle
-    // j uses the row coordinate for hh = 0 and the column coordinate for
-    // hh = 1 with frequency j - hh*D/4 in both modes.  Runtime loops keep
-    // the register footprint small next to the key loop's.
+    // The Q-side pre-pass on the fragments: RMSNorm then rotary in fp32,
+    // rounded once to bf16 (the pre-pass kernel's arithmetic).  Lane (l32,
+    // half) holds dims 16*st + 8*half + i of row l32.  Rotate-half pairs
+    // (m, m + D/2): the partner of register st is register st + D/32 of the
+    // same lane when D/2 is a multiple of 16; for D = 80 it sits in the other
+    // half-wave (register st + 2 + half, read across with v_permlane32_swap).
+    // Angle of pair m: the row coordinate for m < D/4, the column for the
+    // rest, with frequency m mod D/4; it is reduced exactly to a fraction of
+    // a turn before the hardware sine and cosine.  Complex pairs (2j, 2j+1)
+    // lie in one dword of one lane.
     auto transform_q = [&]() {
-      constexpr int HALF = D / 2, QUART = D / 4;
-      const int qrows = min(C::BM, len - qt * C::BM);  // rows of this unit
-      const int r = tid >> 1, hh = tid & 1;
-      const int base_row = qt * C::BM;
-      u16* srow = s_q + r * D;
-      // The previous unit's tiles in the ring must no longer be read.
-      __syncthreads();
-      // 1. stage: each thread copies half a row (D bytes), zeros past the end
-      if (r < C::BM) {
-        const bool ok = r < qrows;
-        const u16* gq = q + size_t(start + base_row + (ok ? r : 0)) * ts.q + size_t(h) * D + hh * HALF;
-#pragma clang loop unroll(disable)
-        for (int c = 0; c < HALF; c += 8) {
-          const u32x4_t v = ok ? *reinterpret_cast<const u32x4_t*>(gq + c) : u32x4_t{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4_t*>(srow + hh * HALF + c) = v;
-        }
-      }
-      __syncthreads();
-      // 2. scale (shared by the two threads of a row) and rotation
-      if (r < C::BM) {
-        const bool rope = qpre.pos != nullptr && r < qrows;
-        float rinv = 1.f;
-        if (qpre.weight != nullptr && r < qrows) {
-          float ss = 0.f;
-          // 16-byte reads: HALF is a multiple of 8 elements
-#pragma clang loop unroll(disable)
-          for (int c = 0; c < HALF; c += 8) {
-            const u32x4_t w4 = *reinterpret_cast<const u32x4_t*>(srow + hh * HALF + c);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float lo = __uint_as_float(w4[i] << 16), hi = __uint_as_float(w4[i] & 0xffff0000u);
-              ss = fmaf(lo, lo, fmaf(hi, hi, ss));
-            }
-          }
-          ss += __shfl_xor(ss, 1);
-          rinv = rsqrtf(ss * (1.f / D) + qpre.eps);
-        }
-        int2 pc = make_int2(0, 0);
-        if (rope) pc = *reinterpret_cast<const int2*>(qpre.pos + 2 * (start + base_row + r));
-        const float coord = float(hh ? pc.y : pc.x);
-        // QUART is a multiple of 4: four independent pairs per iteration keep
-        // their LDS reads and transcendentals overlapped.
-#pragma clang loop unroll_count(4)
-        for (int jj = 0; jj < QUART; ++jj) {
-          const int j = hh * QUART + jj;
-          // the pair's element indices
-          const int ia = qpre.rope_mode == 0 ? j : 2 * j;
-          const int ib = qpre.rope_mode == 0 ? j + HALF : 2 * j + 1;
-          const float a = bf16_bits_to_f32(srow[ia]) * rinv * s_qw[ia];
-          const float bb = bf16_bits_to_f32(srow[ib]) * rinv * s_qw[ib];
-          float ya = a, yb = bb;
-          if (rope) {
-            const float2 rv = s_rev[jj];
-            const float t = coord * rv.x;
-            const float frac = (t - rintf(t)) + (fmaf(coord, rv.x, -t) + coord * rv.y);
-            const float cs = __builtin_amdgcn_cosf(frac), sn = __builtin_amdgcn_sinf(frac);
-            ya = a * cs - bb * sn;
-            yb = bb * cs + a * sn;
-          }
-          srow[ia] = f32_to_bf16_bits(ya);
-          srow[ib] = f32_to_bf16_bits(yb);
-        }
-      }
-      __syncthreads();
-      // 3. fragments from the staged rows
+      constexpr int HALF = D / 2, QUART = D / 4, KS = C::KSTEPS;
+      constexpr bool kCross = HALF % 16 != 0;
+      static_assert(HALF % 8 == 0, "rotary pairs must stay on the same element of a register");
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
-        const u16* sp = s_q + (wave * 32 * QB + 32 * b + l32) * D + half * 8;
+        const int row = row0 + 32 * b + l32;
+        float x[KS][8];
 #pragma unroll
-        for (int st = 0; st < C::KSTEPS; ++st)
-          qf[b][st] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sp + st * 16));
+        for (int st = 0; st < KS; ++st)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[st][i] = float(qf[b][st][i]);
+        if (qpre.weight != nullptr) {
+          float ss = 0.f;
+#pragma unroll
+          for (int st = 0; st < KS; ++st)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = fmaf(x[st][i], x[st][i], ss);
+          ss += other_half(ss);
+          const float rinv = rsqrtf(ss * (1.f / D) + qpre.eps);
+#pragma unroll
+          for (int st = 0; st < KS; ++st)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[st][i] = x[st][i] * rinv * s_qw[16 * st + 8 * half + i];
+        }
+        if (qpre.pos != nullptr) {
+          int2 pc = make_int2(0, 0);
+          if (row < len) pc = *reinterpret_cast<const int2*>(qpre.pos + 2 * (start + row));
+          // cos and sin of the angle of pair index m (< D/2)
+          auto cossin = [&](int m, float& cs, float& sn) {
+            const float coord = float(m < QUART ? pc.x : pc.y);
+            const float2 rv = s_rev[m < QUART ? m : m - QUART];
+            const float t = coord * rv.x;
+            const float frac = (t - rintf(t)) + (fmaf(coord, rv.x, -t) + coord * rv.y);
+            cs = __builtin_amdgcn_cosf(frac);
+            sn = __builtin_amdgcn_sinf(frac);
+          };
+          float y[KS][8];
+          if (qpre.rope_mode == 0) {
+#pragma unroll
+            for (int st = 0; st < KS; ++st) {
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                float partner;
+                if constexpr (kCross) {
+                  // each lane passes on the register its partner lane needs
+                  const int A = (st + HALF / 16 + 1) % KS, B = (st + HALF / 16) % KS;
+                  partner = other_half(half ? x[B][i] : x[A][i]);
+                } else {
+                  partner = x[(st + HALF / 16) % KS][i];
+                }
+                const int d = 16 * st + 8 * half + i;
+                const bool first = d < HALF;
+                float cs, sn;
+                cossin(first ? d : d - HALF, cs, sn);
+                y[st][i] = first ? x[st][i] * cs - partner * sn : x[st][i] * cs + partner * sn;
+              }
+            }
+          } else {
+#pragma unroll
+            for (int st = 0; st < KS; ++st) {
+#pragma unroll
+              for (int i = 0; i < 8; i += 2) {
+                float cs, sn;
+                cossin((16 * st + 8 * half + i) / 2, cs, sn);
+                y[st][i] = x[st][i] * cs - x[st][i + 1] * sn;
+                y[st][i + 1] = x[st][i + 1] * cs + x[st][i] * sn;
+              }
+            }
+          }
+#pragma unroll
+          for (int st = 0; st < KS; ++st)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[st][i] = y[st][i];
+        }
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qf[b][st][i] = (__bf16)x[st][i];
       }
     };
 
@@ -590,10 +594,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       for (int t = 0; t < STAGES - 1; ++t)
         if (t < ntiles) issue_tile(t);
     };
-    // The Q-side pre-pass first (its staging rows use the ring), then the
-    // pass's first tiles.
-    if (q_pending) transform_q();
     start_pass();
+    // The Q-side pre-pass runs while the pass's first tiles are in flight.
+    if (q_pending) transform_q();
 
     auto run_pass = [&](auto m0_tag, auto m_tag, bool started) {
       if (!started) start_pass();

@@ -248,7 +248,7 @@ int vit_varlen_attn_ex(const void* q, const void* k, const void* v, const int32_
  * makes no device or host allocation (no hipMalloc, hipFree or stream-ordered
  * allocation).
  *  - Limit: num_seqs * ceil(max_seqlen / vit_attn_block_m(num_heads, head_dim,
- *    dtype)) at most 262144 work items (the array holds 2 MiB of items);
+ *    dtype)) at most 262144 work items (the array holds 4 MiB of items);
  *    larger calls return VIT_ERR_UNSUPPORTED with nothing enqueued.
  *  - The array exists once per GPU, from the library's load until the process
  *    ends, and every call on that GPU uses it: calls that overlap in time on
@@ -299,14 +299,17 @@ int64_t vit_worklist_capacity(int num_seqs, int max_seqlen, int block_m);
  *  - segments with len_i > 0 that pass validation (enum vit_worklist_error)
  *    are ordered by len_i descending, ties by i ascending (longest first);
  *  - each contributes items (i, j) for j = 0 .. ceil(len_i / block_m) - 1.
- *  items   int32 [cap, 2] (segment, q-tile), written for the first `count` rows.
+ *  items   int32 [cap, 4], 16-byte aligned: row r < count is (segment, q-tile,
+ *          cu_seqlens[segment], length of the segment); rows count ..
+ *          min(cap, count + 2048) - 1 get segment = -1, so the attention
+ *          kernel reads one 16-byte item per work unit and stops at the first
+ *          marked row, without reading the count or cu_seqlens first.
  *  cap     >= vit_worklist_capacity(num_seqs, max_seqlen, block_m).
  *  meta    int32 [2]: meta[0] = count, meta[1] = error bits, both written.
  * Runs entirely on the device (no host sync).  num_seqs at most 8192.
  * The count and the error bits share one caller buffer, and cap is int64, so
- * one allocation of 8 * cap + 8 bytes holds a whole plan and capacities past
- * 2^31 items are expressible; the capacity is still bounded by 2^30 items
- * (VIT_ERR_UNSUPPORTED beyond).
+ * capacities past 2^31 items are expressible; the capacity is still bounded by
+ * 2^30 items (VIT_ERR_UNSUPPORTED beyond).
  */
 int vit_varlen_worklist(const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int block_m,
                         int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream);

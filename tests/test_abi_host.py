@@ -117,6 +117,8 @@ def test_worklist_argument_errors(lib):
     assert f(FAKE, 3, 200, 64, FAKE, 3, meta, None) == 1      # needs 3 * 4 = 12 items
     assert "capacity" in _err(lib)
     assert f(FAKE, 9000, 10, 64, FAKE, 9000, meta, None) == 2
+    assert f(FAKE, 3, 10, 64, FAKE + 4, 3, meta, None) == 1     # items hold 16-byte records
+    assert "16-byte" in _err(lib)
 
 
 def test_planned_argument_errors(lib):

@@ -1,4 +1,10 @@
-"""Device work-list builder vs the CPU rule: bit-exact items, count and error bits."""
+"""Device work-list builder vs the CPU rule: bit-exact items, count and error bits.
+
+Each device item is four int32, (segment, q-tile, first token, length): the
+first two are the list the CPU rule gives; the last two are read off the
+input cu_seqlens; the rows after the count, up to 2048 of them (or the
+capacity), must carry segment -1.
+"""
 import json
 import os
 
@@ -13,15 +19,27 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worklist_cases.json")
 
 
+SENTINEL_SPAN = 2048
+
+
 def _device_list(cu, block_m, max_seqlen, cap=None):
+    """(segment, q-tile) rows, count and error bits of a device list, after
+    checking its other two columns and the marked rows after the count."""
     import torch
     from vision_encoder_varlen_amd import ops
-    cu_t = torch.from_numpy(np.asarray(cu, dtype=np.int32)).cuda()
+    cu = np.asarray(cu, dtype=np.int64)
+    cu_t = torch.from_numpy(cu.astype(np.int32)).cuda()
     plan = ops.varlen_worklist(cu_t, max_seqlen, block_m, cap=cap)
     meta = plan.meta.cpu().numpy()
     count = int(meta[0])
-    items = plan.items.cpu().numpy()[:count]
-    return items, count, int(meta[1])
+    full = plan.items.cpu().numpy()
+    items = full[:count]
+    seg = items[:, 0].astype(np.int64)
+    assert np.array_equal(items[:, 2], cu[seg]), "first-token column"
+    assert np.array_equal(items[:, 3], cu[seg + 1] - cu[seg]), "length column"
+    marked = full[count:min(plan.cap, count + SENTINEL_SPAN)]
+    assert np.all(marked[:, 0] == -1), "rows after the count must carry segment -1"
+    return items[:, :2], count, int(meta[1])
 
 
 def _check(cu, block_m, max_seqlen):

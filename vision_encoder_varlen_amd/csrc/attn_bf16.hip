@@ -188,9 +188,9 @@ __device__ __forceinline__ i16x4_t ds_read_tr16(lds_u16_t* p) {
 template <class C, bool POS_SCALE, bool CAUSAL>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ items,
-    const int32_t* __restrict__ meta, int u_batch, int u_seq_len, int H, float scale_log2,
-    u16* __restrict__ out, float* __restrict__ lse, TokenStrides ts, QPrepass qpre) {
+    const int32_t* __restrict__ items, long long list_cap, int u_batch, int u_seq_len, int H,
+    float scale_log2, u16* __restrict__ out, float* __restrict__ lse, TokenStrides ts,
+    QPrepass qpre) {
   constexpr int D = C::D, BN = C::BN, KB = C::KB, STAGES = C::STAGES, NI = C::NI_HI, QB = C::QB;
   // When D is not a multiple of 32 the last 32-row block of O^T has padding
   // rows; row D then collects the row sums of P (see the tile loop), and
@@ -250,9 +250,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
   }
 
   // items == null: a uniform batch (u_batch segments of u_seq_len tokens).
+  // Otherwise each unit reads its 16-byte item (segment, q-tile, first token,
+  // length) in one load, with no dependent read of the list length or of
+  // cu_seqlens; the list's capacity bounds the loop and the first item marked
+  // with segment -1 ends it.
   const bool uniform = items == nullptr;
   const int uni_tiles = (u_seq_len + C::BM - 1) / C::BM;
-  const int64_t nunits = (uniform ? int64_t(u_batch) * uni_tiles : int64_t(meta[0])) * H;
+  const int64_t nunits = (uniform ? int64_t(u_batch) * uni_tiles : list_cap) * H;
   for (int64_t unit = blockIdx.x; unit < nunits; unit += gridDim.x) {
     // No drain here: the previous unit's output stores may still be in
     // flight.  Every copy wait below counts only copies issued after the
@@ -269,10 +273,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       start = seg * u_seq_len;
       len = u_seq_len;
     } else {
-      const int seg = items[2 * item];
-      qt = items[2 * item + 1];
-      start = cu[seg];
-      len = cu[seg + 1] - start;
+      const int4 it = *reinterpret_cast<const int4*>(items + 4 * size_t(item));
+      if (it.x < 0) break;  // past the list's last item
+      qt = it.y;
+      start = it.z;
+      len = it.w;
     }
     // Causal: a segment's last q-tile visits the most keys, so its tiles are
     // taken last-first (the heaviest items start first, as in the list order).
@@ -674,13 +679,14 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const Schedul
                             : int64_t(sch.batch) * ((sch.seq_len + C::BM - 1) / C::BM);
   const int64_t units = items * int64_t(H);
   if (units <= 0) return hipSuccess;
+  static_assert(kWorklistSentinelSpan >= kMaxAttnGridBf16, "every workgroup must meet a marked item");
   const int64_t grid = units < kMaxAttnGridBf16 ? units : kMaxAttnGridBf16;
   const float c = scale * kLog2e;
   auto kern = causal ? (c > 0.f ? attn_bf16_kernel<C, true, true> : attn_bf16_kernel<C, false, true>)
                     : (c > 0.f ? attn_bf16_kernel<C, true, false> : attn_bf16_kernel<C, false, false>);
   hipExtLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), 0, stream, e0, e1, 0,
                      static_cast<const u16*>(q), static_cast<const u16*>(k),
-                     static_cast<const u16*>(v), sch.cu, sch.items, sch.meta, sch.batch,
+                     static_cast<const u16*>(v), sch.items, (long long)sch.cap, sch.batch,
                      sch.seq_len, H, c, static_cast<u16*>(out), lse, ts, qpre);
   return hipGetLastError();
 }

@@ -54,10 +54,10 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
       start = seg * u_seq_len;
       len = u_seq_len;
     } else {
-      const int seg = items[2 * item];
-      qt = items[2 * item + 1];
-      start = cu[seg];
-      len = cu[seg + 1] - start;
+      const int4 it = *reinterpret_cast<const int4*>(items + 4 * size_t(item));
+      qt = it.y;
+      start = it.z;
+      len = it.w;
     }
     const int qrow = qt * kBM + r;
 

@@ -65,7 +65,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Work-list scratch owned by the library: one buffer per (device, stream), so
-// calls on different streams never share it.  Layout: meta[4] then items.
+// calls on different streams never share it.  Layout: meta[4] then items of
+// four int32 each (16-byte aligned).
 // It grows with stream-ordered allocation (hipFreeAsync of the old buffer and
 // hipMallocAsync of the new one, both on the caller's stream), so a call never
 // waits on the host for work already queued: the old buffer is released only
@@ -98,8 +99,8 @@ int get_scratch(hipStream_t stream, int64_t cap, Scratch** out) {
       s.cap_items = 0;
     }
     int64_t grow = cap < 4096 ? 4096 : cap + cap / 4;
-    e = hipMallocAsync(reinterpret_cast<void**>(&s.buf), size_t(4 + 2 * grow) * sizeof(int32_t),
-                       stream);
+    e = hipMallocAsync(reinterpret_cast<void**>(&s.buf),
+                       size_t(4 + vit::kWorklistItemInts * grow) * sizeof(int32_t), stream);
     if (e != hipSuccess) return hip_fail(e, "hipMallocAsync (work-list scratch)");
     s.cap_items = grow;
   }
@@ -108,12 +109,12 @@ int get_scratch(hipStream_t stream, int64_t cap, Scratch** out) {
 }
 
 // Work-list scratch of vit_varlen_attn_noalloc, for callers that cannot
-// allocate: a fixed device array (meta[4], then kNoAllocMaxItems items of two
-// int32; 2 MiB + 16 B), one copy per GPU, held until the process ends.  In host
+// allocate: a fixed device array (meta[4], then kNoAllocMaxItems items of four
+// int32; 4 MiB + 16 B), one copy per GPU, held until the process ends.  In host
 // code `scratch` names a host-side stand-in, not device memory: host code uses
 // only the address hipGetSymbolAddress returns for the current device.
 constexpr int64_t kNoAllocMaxItems = int64_t(1) << 18;
-static __device__ __align__(256) int32_t scratch[4 + 2 * kNoAllocMaxItems];
+static __device__ __align__(256) int32_t scratch[4 + vit::kWorklistItemInts * kNoAllocMaxItems];
 
 constexpr int kNoAllocMaxDevices = 64;
 std::mutex g_noalloc_mu;
@@ -340,8 +341,9 @@ int check_worklist_args(const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
   if (cap < need)
     return fail(VIT_ERR_INVALID_ARG, "cap %lld below the required capacity %lld", (long long)cap,
                 (long long)need);
-  if (!aligned4(cu_seqlens) || !aligned4(items) || !aligned4(meta))
+  if (!aligned4(cu_seqlens) || !aligned4(meta))
     return fail(VIT_ERR_INVALID_ARG, "int32 buffers must be 4-byte aligned");
+  if (!aligned16(items)) return fail(VIT_ERR_INVALID_ARG, "items must be 16-byte aligned");
   return VIT_OK;
 }
 
@@ -501,6 +503,7 @@ int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
                             hipStream_t stream) {
   const TimingHook t = take_timing();
   if (!items || !meta) return fail(VIT_ERR_INVALID_ARG, "null work-list pointer");
+  if (!aligned16(items)) return fail(VIT_ERR_INVALID_ARG, "items must be 16-byte aligned");
   if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   int rc = check_attn_args(q, k, v, cu_seqlens, 0, 0, num_heads, head_dim, scale, out);
   if (rc != VIT_OK) return rc;
@@ -527,6 +530,7 @@ int vit_varlen_attn_planned_qnorm_rope(
     void* out, float* lse, const int64_t* strides, hipStream_t stream) {
   const TimingHook t = take_timing();
   if (!items || !meta) return fail(VIT_ERR_INVALID_ARG, "null work-list pointer");
+  if (!aligned16(items)) return fail(VIT_ERR_INVALID_ARG, "items must be 16-byte aligned");
   if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   int rc = check_attn_args(q, k, v, cu_seqlens, 0, 0, num_heads, head_dim, scale, out);
   if (rc != VIT_OK) return rc;

@@ -52,7 +52,7 @@ struct QPrepass {
 // seq_len), never stored), taken in index order.
 struct Schedule {
   const int32_t* cu;
-  const int32_t* items;
+  const int32_t* items;  // int32 [cap, 4]: (segment, q-tile, first token, length)
   const int32_t* meta;
   int64_t cap;  // list capacity (work-list form)
   int batch;    // uniform form
@@ -69,6 +69,8 @@ constexpr int kBlockMF32 = 32;  // 1 wave, lane pairs share a row, fp32 kernel
 
 // Work-list builder limits: one workgroup sorts every segment in LDS.
 constexpr int kWorklistMaxSeqs = 8192;
+// Work items are (segment, q-tile, first token, length), four int32 each.
+constexpr int kWorklistItemInts = 4;
 
 // Largest span of one segment's rows in a k or v tensor (bytes) that the
 // bf16 attention kernel addresses with 32-bit buffer offsets, counted with the
@@ -88,6 +90,12 @@ constexpr int64_t kMaxAttnGrid = int64_t(1) << 22;
 // units share one workgroup's set-up (copy offsets, LDS tables): 12% faster
 // on 2048 segments of 64 tokens, unchanged on the long-segment batches.
 constexpr int64_t kMaxAttnGridBf16 = 2048;
+// The builder marks this many entries after the last item (or all of the
+// list, if shorter) with segment -1.  A bf16 attention workgroup reads items
+// b/H, (b + grid)/H, ... (grid <= kMaxAttnGridBf16) and stops at the first
+// marked one, which lies within grid/H entries of the count, so it never needs
+// the count itself.
+constexpr int64_t kWorklistSentinelSpan = kMaxAttnGridBf16;
 
 inline bool attn_head_dim_supported(int D) {
   return D == 32 || D == 64 || D == 80 || D == 96 || D == 128;

@@ -39,7 +39,10 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* tot
 
 // Builds the list with THREADS threads of one workgroup.  keys and offs are
 // LDS arrays of npad entries (npad = next power of two >= N), s_wave an LDS
-// array of THREADS / 64 ints.
+// array of THREADS / 64 ints.  Item i is four int32 at items + 4i:
+// (segment, q-tile, first token cu[segment], length); items
+// [count, min(cap, count + kWorklistSentinelSpan)) get segment -1, so an
+// attention workgroup can read its item without first reading the count.
 template <int THREADS>
 __device__ __forceinline__ void build_worklist(const int32_t* __restrict__ cu, int N, int npad,
                                                int max_seqlen, int block_m,
@@ -125,11 +128,17 @@ __device__ __forceinline__ void build_worklist(const int32_t* __restrict__ cu, i
       const int len = int(0x7fffffffu - static_cast<unsigned>(key >> 32));
       const int nt = (len + block_m - 1) / block_m;
       const int base = offs[i];
-      for (int j = 0; j < nt; ++j) {
-        items[2 * (base + j)] = seg;
-        items[2 * (base + j) + 1] = j;
-      }
+      const int first = cu[seg];
+      for (int j = 0; j < nt; ++j)
+        *reinterpret_cast<int4*>(items + 4 * (long long)(base + j)) = make_int4(seg, j, first, len);
     }
+  }
+  // Sentinels after the last item (from the start when the list is empty).
+  {
+    const long long from = overflow ? 0 : static_cast<long long>(total);
+    const long long to = from + kWorklistSentinelSpan < cap ? from + kWorklistSentinelSpan : cap;
+    for (long long i = from + tid; i < to; i += THREADS)
+      *reinterpret_cast<int4*>(items + 4 * i) = make_int4(-1, 0, 0, 0);
   }
   if (tid == 0) {
     meta[0] = overflow ? 0 : total;

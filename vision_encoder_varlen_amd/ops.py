@@ -265,7 +265,9 @@ def varlen_worklist(cu_seqlens: torch.Tensor, max_seqlen: int, block_m: int,
     if need < 0:
         raise ValueError("bad work-list sizes")
     cap = need if cap is None else int(cap)
-    items = torch.empty((max(cap, 1), 2), dtype=torch.int32, device=cu_seqlens.device)
+    # (segment, q-tile, first token, length) per item; torch's allocations are
+    # 256-byte aligned, which the 16-byte item reads need.
+    items = torch.empty((max(cap, 1), 4), dtype=torch.int32, device=cu_seqlens.device)
     meta = torch.empty(2, dtype=torch.int32, device=cu_seqlens.device)
     _lib.check(_lib.load().vit_varlen_worklist(
         cu_seqlens.data_ptr(), n, int(max_seqlen), int(block_m), items.data_ptr(), cap,

@@ -2,8 +2,8 @@
 
 The bf16 attention grid is capped at 2048 workgroups; beyond that each
 workgroup loops over several (segment, q-tile, head) units, reusing its LDS
-ring, its Q staging rows (q-side pre-pass) and its copy offsets, and letting a
-unit's output stores drain under the next unit's loads.  These batches have
+ring and its copy offsets, and letting a unit's output stores drain under the
+next unit's loads.  These batches have
 several thousand units of mixed kinds (multi-tile segments, ragged last tiles,
 64-key single tiles, empty segments) so that every workgroup runs two or more
 of them, through each entry point that launches the kernel: the plain call,
@@ -72,8 +72,8 @@ def test_multi_unit_workgroups(D):
 @pytest.mark.parametrize("D", [80, 128])
 def test_multi_unit_workgroups_fused_q(D):
     """The planned call with q's norm and rotary inside the kernel: each unit
-    stages its query rows in the workgroup's LDS ring after the previous
-    unit's last tile."""
+    normalises and rotates its Q fragments in registers while its first K/V
+    tiles are in flight behind the previous unit's stores."""
     import torch
     from vision_encoder_varlen_amd import ops
     H = 8
@@ -102,3 +102,36 @@ def test_multi_unit_workgroups_fused_q(D):
     eq, ek = oracle.round_to_bf16(eq), oracle.round_to_bf16(ek)
     want = oracle.varlen_attention(eq, ek, x.v, x.cu_seqlens, wl.softmax_scale)
     assert_attn_close(to_host(out), want, "bf16", f"multi-unit fused q D={D}")
+
+
+@pytest.mark.parametrize("H,D", [(12, 64), (6, 128), (3, 80)])
+def test_multi_unit_head_major_order(H, D):
+    """Head counts that are not a multiple of 8 take the units head-major, in
+    one contiguous chunk per XCD, reading the list length; more units than
+    the grid, so each workgroup runs several, through the list (plain and
+    causal) and the uniform batch."""
+    import torch
+    from vision_encoder_varlen_amd import ops
+    lens = _lengths(700 + H, n=48 * 8 // H * 8)
+    wl = W.from_seqlens(lens, H=H, D=D, dtype="bf16", seed=800 + H)
+    x = W.generate(wl)
+    assert _units(lens, H) > 2 * GRID_CAP
+    q, k, v = (to_dev(a, "bf16") for a in (x.q, x.k, x.v))
+    cu = torch.from_numpy(x.cu_seqlens).cuda()
+    out, out_c = torch.full_like(q, float("nan")), torch.full_like(q, float("nan"))
+    ops.varlen_attn(q, k, v, cu, wl.max_seqlen, out=out)
+    ops.varlen_attn(q, k, v, cu, wl.max_seqlen, causal=True, out=out_c)
+    torch.cuda.synchronize()
+    want = oracle.varlen_attention(x.q, x.k, x.v, x.cu_seqlens, wl.softmax_scale)
+    assert_attn_close(to_host(out), want, "bf16", f"head-major H={H} D={D}")
+    want_c = oracle.varlen_attention(x.q, x.k, x.v, x.cu_seqlens, wl.softmax_scale, causal=True)
+    assert_attn_close(to_host(out_c), want_c, "bf16", f"head-major causal H={H} D={D}")
+    # uniform batch: 600 segments of 100 tokens
+    wu = W.from_seqlens([100] * 600, H=H, D=D, dtype="bf16", seed=900 + H)
+    xu = W.generate(wu)
+    qu, ku, vu = (to_dev(a, "bf16") for a in (xu.q, xu.k, xu.v))
+    dense = torch.full_like(qu, float("nan"))
+    ops.dense_batch_attn(qu, ku, vu, 600, 100, out=dense)
+    torch.cuda.synchronize()
+    want_u = oracle.dense_batch_attention(xu.q, xu.k, xu.v, 600, 100, wu.softmax_scale)
+    assert_attn_close(to_host(dense), want_u, "bf16", f"head-major uniform H={H} D={D}")

@@ -188,7 +188,8 @@ __device__ __forceinline__ i16x4_t ds_read_tr16(lds_u16_t* p) {
 template <class C, bool POS_SCALE, bool CAUSAL>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-    const int32_t* __restrict__ items, long long list_cap, int u_batch, int u_seq_len, int H,
+    const int32_t* __restrict__ items, const int32_t* __restrict__ meta, long long list_cap,
+    int u_batch, int u_seq_len, int H,
     float scale_log2, u16* __restrict__ out, float* __restrict__ lse, TokenStrides ts,
     QPrepass qpre) {
   constexpr int D = C::D, BN = C::BN, KB = C::KB, STAGES = C::STAGES, NI = C::NI_HI, QB = C::QB;
@@ -254,18 +255,43 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
   // length) in one load, with no dependent read of the list length or of
   // cu_seqlens; the list's capacity bounds the loop and the first item marked
   // with segment -1 ends it.
+  //
+  // Unit order.  A unit is an (item, head) pair.  Workgroup b runs on XCD
+  // b % 8 (the dispatcher hands workgroups to the 8 XCDs in turn; the grid is
+  // a multiple of 8, so a workgroup keeps its XCD from unit to unit), and
+  // each XCD has its own L2.  With H a multiple of 8 the item-major order
+  // (unit = item * H + head) gives XCD x the heads h = x (mod 8) of every
+  // item, so its co-resident workgroups share those heads' K and V tiles.
+  // With other head counts (12, say) that order would spread every head over
+  // several XCDs; the units are then taken head-major (head * N + item, N
+  // items) in 8 contiguous chunks, one per XCD, so each XCD streams about H/8
+  // heads, one after another, and needs the list length N itself.
   const bool uniform = items == nullptr;
   const int uni_tiles = (u_seq_len + C::BM - 1) / C::BM;
-  const int64_t nunits = (uniform ? int64_t(u_batch) * uni_tiles : list_cap) * H;
-  for (int64_t unit = blockIdx.x; unit < nunits; unit += gridDim.x) {
+  const bool head_major = (H & 7) != 0;
+  const int64_t n_items =
+      uniform ? int64_t(u_batch) * uni_tiles : (head_major ? int64_t(meta[0]) : list_cap);
+  const int64_t nunits = n_items * H;
+  const int64_t xcd_chunk = (nunits + 7) / 8;
+  for (int64_t slot = blockIdx.x;; slot += gridDim.x) {
     // No drain here: the previous unit's output stores may still be in
     // flight.  Every copy wait below counts only copies issued after the
     // tile it waits for, and loads (global and global -> LDS) complete in
     // issue order, so older outstanding stores can only lengthen a wait,
     // never end it early.  (Letting the stores drain under this unit's
     // loads is 4% faster on batches of 64-token segments.)
-    const int item = int(unit / H);
-    const int h = int(unit - int64_t(item) * H);
+    int item, h;
+    if (head_major) {
+      const int64_t s = slot >> 3;
+      const int64_t u = int64_t(blockIdx.x & 7) * xcd_chunk + s;
+      if (s >= xcd_chunk || u >= nunits) break;
+      h = int(u / n_items);
+      item = int(u - int64_t(h) * n_items);
+    } else {
+      if (slot >= nunits) break;
+      item = int(slot / H);
+      h = int(slot - int64_t(item) * H);
+    }
     int qt, start, len;
     if (uniform) {
       const int seg = item / uni_tiles;
@@ -680,13 +706,15 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const Schedul
   const int64_t units = items * int64_t(H);
   if (units <= 0) return hipSuccess;
   static_assert(kWorklistSentinelSpan >= kMaxAttnGridBf16, "every workgroup must meet a marked item");
-  const int64_t grid = units < kMaxAttnGridBf16 ? units : kMaxAttnGridBf16;
+  static_assert(kMaxAttnGridBf16 % 8 == 0, "the grid is a whole number of XCD rounds");
+  // A multiple of 8 workgroups, so each keeps its XCD across its units.
+  const int64_t grid = ((units < kMaxAttnGridBf16 ? units : kMaxAttnGridBf16) + 7) / 8 * 8;
   const float c = scale * kLog2e;
   auto kern = causal ? (c > 0.f ? attn_bf16_kernel<C, true, true> : attn_bf16_kernel<C, false, true>)
                     : (c > 0.f ? attn_bf16_kernel<C, true, false> : attn_bf16_kernel<C, false, false>);
   hipExtLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), 0, stream, e0, e1, 0,
                      static_cast<const u16*>(q), static_cast<const u16*>(k),
-                     static_cast<const u16*>(v), sch.items, (long long)sch.cap, sch.batch,
+                     static_cast<const u16*>(v), sch.items, sch.meta, (long long)sch.cap, sch.batch,
                      sch.seq_len, H, c, static_cast<u16*>(out), lse, ts, qpre);
   return hipGetLastError();
 }

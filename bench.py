@@ -1,9 +1,13 @@
 """Benchmark: one step = the whole hot path on one packed batch.
 
-Step = Q/K RMSNorm + 2D RoPE pre-pass (in place on q and k) and work-list
-build (one launch, vit_qk_norm_rope_worklist), then varlen attention
-(vit_varlen_attn_planned) -- enqueued on the current stream through the C ABI,
-with inputs resident in HBM before timing starts.
+Step = Q/K RMSNorm + 2D RoPE pre-pass and work-list build (one launch,
+vit_qk_norm_rope_into: from the projection's q and k, which stay unchanged,
+into the attention's q and k), then varlen attention (vit_varlen_attn_planned)
+-- enqueued on the current stream through the C ABI, with inputs resident in
+HBM before timing starts.  Every step thus normalises the same rows; a pre-pass
+in place would normalise its own output again each step, and repeated RMSNorm
+with unequal weights drives the rows towards their largest-weight channels
+(near-zero MFMA operands, which run faster than real data).
 
 Default workload: 4 images of 32x32 patches (4096 tokens), 16 heads, head dim
 80, bf16, RoPE only (the workload the attention metric is quoted on).  The
@@ -15,6 +19,11 @@ loop with HIP events that the kernel's dispatch records at its start and end
 taken against MI355X's dense bf16 MFMA peak.  With the default workload the
 line also carries the attention kernel alone on the ragged 24-image batch
 (second_target), the other workload the 50%-of-peak target is set on.
+
+Before the W warm-up steps the step runs untimed for at least --settle-ms
+(default 1 s, reported under "settle"): the chip's clock climbs for a few
+hundred milliseconds of sustained load, and the timed steps are meant to run at
+the clock it holds in continuous use.
 
 Memory-bound side timings (the pre-pass, and the attention once more) read a
 1 GiB buffer before each launch, so their inputs come from HBM rather than
@@ -74,6 +83,11 @@ def parse():
                    help="with the default workload (2): also time the attention kernel alone on "
                         "seeded workload N (default 3, the ragged batch; 0 = off) and report it "
                         "under second_target")
+    p.add_argument("--settle-ms", type=float, default=1000.0,
+                   help="untimed steps for at least this many milliseconds before the warm-up "
+                        "steps (and before the second target's launches): the chip raises its "
+                        "clock over the first few hundred ms of sustained load, and the timed "
+                        "steps should run at the clock it then holds")
     p.add_argument("--flush-mib", type=int, default=1024,
                    help="size of the buffer read before each memory-bound side-loop launch, "
                         "so its inputs come from HBM and not the 256 MB Infinity Cache")
@@ -95,14 +109,17 @@ def parse():
 
 
 def _counter_rows(path, counter):
-    """(kernel name, grid size, value in KiB) per dispatch of one rocprofv3 counter CSV."""
+    """(kernel name, grid size, value in KiB) per dispatch of one rocprofv3
+    counter CSV, in dispatch order."""
     import csv
     rows = []
     with open(path, newline="") as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] == counter:
-                rows.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
-    return rows
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]),
+                             float(r["Counter_Value"])))
+    rows.sort()
+    return [r[1:] for r in rows]
 
 
 def summarize_pmc(args):
@@ -120,13 +137,20 @@ def summarize_pmc(args):
             raise SystemExit("no copy-kernel dispatch in the counter CSV (run with --copy-calibration)")
         return max(c[2] for c in copies)
 
+    meta = json.load(open(args.calibration_meta))
+    first, count = meta["timed_dispatches"]
+
     def attn(rows):
-        vals = [r[2] for r in rows if "attn_bf16_kernel" in r[0] or "attn_f32_kernel" in r[0]]
-        if not vals:
+        """Mean over the timed steps' attention dispatches."""
+        names = [r[0] for r in rows if "attn_bf16_kernel" in r[0] or "attn_f32_kernel" in r[0]]
+        if not names:
             raise SystemExit("no attention dispatch in the counter CSV")
+        vals = [r[2] for r in rows if r[0] == names[0]][first:first + count]
+        if len(vals) != count:
+            raise SystemExit(f"expected {count} timed attention dispatches after {first}, "
+                             f"found {len(vals)}")
         return float(np.mean(vals)), len(vals)
 
-    meta = json.load(open(args.calibration_meta))
     known_kib = meta["copy_mib"] * 1024.0
     f_fetch = known_kib / calib(fetch)
     f_write = known_kib / calib(write)
@@ -141,7 +165,9 @@ def summarize_pmc(args):
         "algorithmic_bytes_per_launch": meta["algorithmic_bytes"],
         "raw_kib_per_launch": {"FETCH_SIZE": fk, "WRITE_SIZE": wk},
         "calibration": {"copy_mib": meta["copy_mib"], "fetch_factor": f_fetch, "write_factor": f_write},
-        "dispatches": {"FETCH_SIZE": nf, "WRITE_SIZE": nw},
+        "dispatches": {"FETCH_SIZE": nf, "WRITE_SIZE": nw,
+                       "which": f"the timed steps' attention launches: ordinals {first} to "
+                                f"{first + count - 1} of the step's attention kernel"},
         "command": args.pmc_command,
     }
     with open(args.traffic_json or _traffic_path(meta["workload"]), "w") as f:
@@ -255,23 +281,33 @@ def main():
     wl = W.config(args.config)
     x = W.generate(wl)
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    import ctypes
+    # The step's inputs as a QKV projection leaves them (q_src, k_src, v), and
+    # the attention's q and k, which the pre-pass writes from them every step:
+    # the sources stay unchanged, so every step normalises and rotates the
+    # same rows.
     if args.packed_qkv:
-        # q, k, v as views of one packed [T, 3, H, D] projection output.
+        # q_src, k_src, v as views of one packed [T, 3, H, D] projection output.
         qkv = torch.from_numpy(np.stack([x.q, x.k, x.v], axis=1)).to(tdt).to(dev)
-        q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+        q_src, k_src, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
     else:
-        q, k, v = (torch.from_numpy(a).to(tdt).to(dev) for a in (x.q, x.k, x.v))
+        q_src, k_src, v = (torch.from_numpy(a).to(tdt).to(dev) for a in (x.q, x.k, x.v))
+    q = torch.empty(q_src.shape, dtype=tdt, device=dev)
+    k = torch.empty(k_src.shape, dtype=tdt, device=dev)
     pos = torch.from_numpy(x.pos).to(dev)
     cu = torch.from_numpy(x.cu_seqlens).to(dev)
     wq = torch.from_numpy(x.wq).to(dev) if wl.use_norm else None
     wk = torch.from_numpy(x.wk).to(dev) if wl.use_norm else None
+    wq_p = wq.data_ptr() if wq is not None else None
+    wk_p = wk.data_ptr() if wk is not None else None
     out = torch.empty(q.shape, dtype=tdt, device=dev)
     T, H, D = q.shape
-    # Token strides (elements) of q, k, v, out; None = contiguous [T, H, D].
-    strides_arr = None
+    # Token strides (elements): of q_src, k_src for the pre-pass, of q, k, v,
+    # out for the attention; None = contiguous [T, H, D].
+    src_strides = at_strides = None
     if args.packed_qkv:
-        import ctypes
-        strides_arr = (ctypes.c_int64 * 4)(q.stride(0), k.stride(0), v.stride(0), H * D)
+        src_strides = (ctypes.c_int64 * 2)(q_src.stride(0), k_src.stride(0))
+        at_strides = (ctypes.c_int64 * 4)(H * D, H * D, v.stride(0), H * D)
     dcode = ops.dtype_code(tdt)
     bm = ops.attn_block_m(H, D, tdt)
     plan = ops.varlen_worklist(cu, wl.max_seqlen, bm)
@@ -281,47 +317,51 @@ def main():
     sh = stream.cuda_stream
     check = _lib.check
     # Precomputed ctypes arguments keep host overhead per step far below GPU time.
-    pre_args = (q.data_ptr(), k.data_ptr(), T, H, D, dcode, pos.data_ptr(), float(wl.theta),
-                wq.data_ptr() if wq is not None else None, wk.data_ptr() if wk is not None else None,
-                float(wl.eps), strides_arr, sh)
+    no_list = (None, 0, 0, 0, None, 0, None)
     wl_args = (cu.data_ptr(), wl.num_seqs, wl.max_seqlen, bm, plan.items.data_ptr(), plan.cap,
                plan.meta.data_ptr(), sh)
+    # vit_qk_norm_rope_into: the pre-pass alone, and (the step's first
+    # launch) the pre-pass with the work-list build; rope_mode 0: rotate-half.
+    f_pre = f_fused = lib.vit_qk_norm_rope_into
+    pre_head = (q_src.data_ptr(), k_src.data_ptr(), src_strides, q.data_ptr(), k.data_ptr(), T, H,
+                D, dcode, pos.data_ptr(), float(wl.theta), wq_p, wk_p, float(wl.eps), 0, None)
+    pre_args = pre_head + no_list + (sh,)
+    fused_args = pre_head + wl_args
+    f_wl, f_at = lib.vit_varlen_worklist, lib.vit_varlen_attn_planned
     flags = 1 if args.causal else 0     # VIT_ATTN_CAUSAL
     at_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), cu.data_ptr(), plan.items.data_ptr(),
                plan.cap, plan.meta.data_ptr(), H, D, float(wl.softmax_scale), dcode, flags,
-               out.data_ptr(), None, strides_arr, sh)
+               out.data_ptr(), None, at_strides, sh)
     # The same attention call that also writes the log-sum-exp rows (timed
     # outside the timed loop, for its overhead).
     lse_buf = torch.empty((T, H), dtype=torch.float32, device=dev)
-    at_lse_args = at_args[:-3] + (lse_buf.data_ptr(), strides_arr, sh)
-    # The step's first launch: pre-pass and work-list build together.
-    fused_args = pre_args[:11] + (0, strides_arr) + wl_args   # rope_mode 0: rotate-half
-    f_pre, f_wl, f_at = lib.vit_qk_norm_rope_strided, lib.vit_varlen_worklist, lib.vit_varlen_attn_planned
+    at_lse_args = at_args[:-3] + (lse_buf.data_ptr(), at_strides, sh)
     if args.dense_batch:
         lens = np.diff(x.cu_seqlens)
         if len(set(lens.tolist())) != 1:
             sys.exit("bench: --dense-batch needs a workload of equal-length segments")
         f_at = lib.vit_dense_batch_attn
         at_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), wl.num_seqs, int(lens[0]), H, D,
-                   float(wl.softmax_scale), dcode, flags, out.data_ptr(), None, strides_arr, sh)
-        at_lse_args = at_args[:-3] + (lse_buf.data_ptr(), strides_arr, sh)
-    f_fused = lib.vit_qk_norm_rope_worklist
+                   float(wl.softmax_scale), dcode, flags, out.data_ptr(), None, at_strides, sh)
+        at_lse_args = at_args[:-3] + (lse_buf.data_ptr(), at_strides, sh)
     if args.fuse_q:
         if args.dense_batch:
             sys.exit("bench: --fuse-q times the work-list step; drop --dense-batch")
         # k's pre-pass with the work-list build in one launch; q's RMSNorm and
-        # rotary inside the attention kernel.
-        wk_p = wk.data_ptr() if wk is not None else None
-        wq_p = wq.data_ptr() if wq is not None else None
-        pre_args = (None, k.data_ptr(), T, H, D, dcode, pos.data_ptr(), float(wl.theta), None, wk_p,
-                    float(wl.eps), strides_arr, sh)
-        fused_args = pre_args[:11] + (0, strides_arr) + wl_args
+        # rotary inside the attention kernel, which reads q_src as it is.
+        pre_head = (None, k_src.data_ptr(), src_strides, None, k.data_ptr(), T, H, D, dcode,
+                    pos.data_ptr(), float(wl.theta), None, wk_p, float(wl.eps), 0, None)
+        pre_args = pre_head + no_list + (sh,)
+        fused_args = pre_head + wl_args
         f_at = lib.vit_varlen_attn_planned_qnorm_rope
-        at_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), cu.data_ptr(), plan.items.data_ptr(),
-                   plan.cap, plan.meta.data_ptr(), H, D, float(wl.softmax_scale), dcode, flags,
-                   pos.data_ptr(), float(wl.theta), wq_p, float(wl.eps), 0,
-                   out.data_ptr(), None, strides_arr, sh)
-        at_lse_args = at_args[:-3] + (lse_buf.data_ptr(), strides_arr, sh)
+        fq_strides = None
+        if args.packed_qkv:
+            fq_strides = (ctypes.c_int64 * 4)(q_src.stride(0), H * D, v.stride(0), H * D)
+        at_args = (q_src.data_ptr(), k.data_ptr(), v.data_ptr(), cu.data_ptr(),
+                   plan.items.data_ptr(), plan.cap, plan.meta.data_ptr(), H, D,
+                   float(wl.softmax_scale), dcode, flags, pos.data_ptr(), float(wl.theta), wq_p,
+                   float(wl.eps), 0, out.data_ptr(), None, fq_strides, sh)
+        at_lse_args = at_args[:-3] + (lse_buf.data_ptr(), fq_strides, sh)
 
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -331,11 +371,6 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-        if args.calibration_meta:
-            with open(args.calibration_meta, "w") as f:
-                json.dump({"copy_mib": args.copy_calibration, "workload": wl.name,
-                           "kernel_source_sha": _kernel_sha(),
-                           "algorithmic_bytes": 4 * T * H * D * q.element_size()}, f)
 
     K, Wm = args.steps, args.warmup
     f_hook = lib.vit_time_next_kernel
@@ -362,6 +397,7 @@ def main():
             check(f_hook(e[0].cuda_event, e[1].cuda_event))
         check(f_at(*at_args))
 
+    settle_steps, settle_ms = settle(step, args.settle_ms, torch)
     for _ in range(Wm):
         step()
     torch.cuda.synchronize()
@@ -373,6 +409,16 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
+    if args.copy_calibration > 0 and args.calibration_meta:
+        # the timed steps' attention launches, as ordinals among the dispatches
+        # of the step's attention kernel (the first attention kernel the run
+        # dispatches): the settle and warm-up steps come before them, the
+        # side loops after
+        with open(args.calibration_meta, "w") as f:
+            json.dump({"copy_mib": args.copy_calibration, "workload": wl.name,
+                       "kernel_source_sha": _kernel_sha(),
+                       "algorithmic_bytes": 4 * T * H * D * q.element_size(),
+                       "timed_dispatches": [settle_steps + Wm, K]}, f)
     ms_per_step = total_ms / K
     attn_avg_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev if e is not None]))
 
@@ -449,6 +495,8 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": Wm,
+        "settle": {"steps": settle_steps, "ms": round(settle_ms, 1),
+                   "note": "untimed steps before the warm-up steps, until the clock has ramped"},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -500,7 +548,7 @@ def main():
     if args.second_target and args.config == 2 and not (args.causal or args.fuse_q or args.dense_batch
                                                          or args.packed_qkv):
         result["second_target"] = second_target(args.second_target, lib, torch, dev, stream,
-                                                max(K, 50), new_events)
+                                                max(K, 50), new_events, args.settle_ms)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, args.causal)
         if not args.no_oracle_per_config:
@@ -508,7 +556,23 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def second_target(n, lib, torch, dev, stream, launches, new_events):
+def settle(step, ms, torch):
+    """Run `step` untimed, in groups of 10 with a synchronisation after each,
+    until at least `ms` milliseconds of wall time have passed; returns the
+    number of steps and the milliseconds taken.  Under sustained load the
+    chip's clock climbs for a few hundred milliseconds: MFMA-bound launches
+    of the 1 x 16384 workload run about 1.53 ms at first and 1.21 ms once it
+    has settled."""
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+    return n, (time.perf_counter() - t0) * 1e3
+
+
+def second_target(n, lib, torch, dev, stream, launches, new_events, settle_ms):
     """The attention kernel alone on seeded workload n, as the step runs it
     (pre-pass applied once, then the planned attention): its own dispatch
     duration over `launches` launches, and the fraction of bf16 MFMA peak."""
@@ -529,8 +593,8 @@ def second_target(n, lib, torch, dev, stream, launches, new_events):
     at_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), cu.data_ptr(), plan.items.data_ptr(),
                plan.cap, plan.meta.data_ptr(), H, D, float(wl.softmax_scale), _lib.VIT_BF16, 0,
                out.data_ptr(), None, None, sh)
-    for _ in range(5):
-        _lib.check(lib.vit_varlen_attn_planned(*at_args))
+    settled, settled_ms = settle(lambda: _lib.check(lib.vit_varlen_attn_planned(*at_args)),
+                                 settle_ms, torch)
     evs = [new_events(2) for _ in range(launches)]
     torch.cuda.synchronize()
     for e in evs:
@@ -545,6 +609,7 @@ def second_target(n, lib, torch, dev, stream, launches, new_events):
     ach = wl.attn_flops / (avg * 1e-3) / 1e12
     return {"workload": wl.name, "tokens": T, "heads": H, "head_dim": D, "images": wl.num_seqs,
             "flops_per_launch": wl.attn_flops, "launches": launches,
+            "settle": {"launches": settled, "ms": round(settled_ms, 1)},
             "attention_avg_us": round(avg * 1e3, 3), "attention_median_us": round(med * 1e3, 3),
             "achieved": round(ach, 3), "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
             "frac": round(ach / PEAK_BF16_TFLOPS, 4),

@@ -163,6 +163,35 @@ int vit_qk_norm_rope_worklist(void* q, void* k, int64_t total_tokens, int num_he
                               int32_t* meta, hipStream_t stream);
 
 /*
+ * vit_qk_norm_rope_worklist out of place: q and k receive the normalised and
+ * rotated rows of q_src and k_src, which are only read.  This is the form the
+ * step takes on the vLLM page (_qkv_with_rope in _VisionAttentionBase): the
+ * norm and the rotary make new q and k from the views of the QKV projection's
+ * output, which stays as it was.  With neither norm nor rotary requested the
+ * rows are copied.
+ *
+ *  q_src, k_src  [total_tokens, H, D] of `dtype`, token strides src_strides[0]
+ *                and src_strides[1] (null: contiguous); q_src is null exactly
+ *                when q is.
+ *  q, k          the outputs, token strides strides[0], strides[1].  Each is
+ *                either its own source (the same pointer and stride: the
+ *                in-place call) or shares no byte with q_src or k_src; other
+ *                overlaps are VIT_ERR_INVALID_ARG.
+ *  cu_seqlens, items, meta
+ *                all null: no work-list is built (num_seqs, max_seqlen,
+ *                block_m and cap are then ignored); all given: as for
+ *                vit_qk_norm_rope_worklist; a mix is VIT_ERR_INVALID_ARG.
+ * Everything else as for vit_qk_norm_rope_worklist, and errors as for it
+ * (checked before anything is enqueued).
+ */
+int vit_qk_norm_rope_into(const void* q_src, const void* k_src, const int64_t* src_strides,
+                          void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
+                          int dtype, const int32_t* pos, float theta, const float* q_weight,
+                          const float* k_weight, float eps, int rope_mode, const int64_t* strides,
+                          const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int block_m,
+                          int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream);
+
+/*
  * Varlen attention, bf16 in and out, fp32 accumulation and softmax.
  *
  * For every segment i, head h and query a in the segment:
@@ -341,7 +370,7 @@ int vit_varlen_attn_planned(const void* q, const void* k, const void* v,
  * and feeds the result to the MFMAs.  q in memory is not modified.  This is
  * _qkv_with_rope (vLLM page: norm, then rotary) with q's read and write of the
  * separate pre-pass removed; k is still prepared by vit_qk_norm_rope_ex (or
- * vit_qk_norm_rope_worklist) called with q = null.
+ * vit_qk_norm_rope_worklist, or vit_qk_norm_rope_into) called with q = null.
  *  pos        int32 [T, 2] (row, col), 8-byte aligned, or null.
  *  q_weight   fp32 [D], 16-byte aligned, or null.
  *  theta, eps, rope_mode   as for vit_qk_norm_rope_ex (checked when used).

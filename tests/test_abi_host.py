@@ -109,6 +109,37 @@ def test_prepass_argument_errors(lib):
     assert f(FAKE, FAKE + 0x100, 0, 2, 64, 1, FAKE, 10000.0, None, None, 1e-6, None) == 0
 
 
+def test_prepass_into_argument_errors(lib):
+    """The out-of-place pre-pass: every rejection happens before any launch.
+    T = 4 tokens of H = 2, D = 64 bf16 span 1 KiB per tensor."""
+    import ctypes
+    f = lib.vit_qk_norm_rope_into
+    qs, ks, q, k = FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000
+    none_list = (None, 0, 0, 0, None, 0, None, None)
+
+    def call(q_src, k_src, qq, kk, T=4, src_strides=None, strides=None, pos=FAKE, lst=none_list):
+        return f(q_src, k_src, src_strides, qq, kk, T, 2, 64, 1, pos, 10000.0, None, None, 1e-6, 0,
+                 strides, *lst)
+
+    assert call(None, ks, q, k) == 1 and "both" in _err(lib)
+    assert call(qs, ks, None, k) == 1
+    assert call(qs, None, q, k) == 1 and "k_src" in _err(lib)
+    assert call(qs + 8, ks, q, k) == 1 and "aligned" in _err(lib)
+    # an output overlapping a source it is not
+    assert call(qs, ks, qs + 0x200, k) == 1 and "overlaps" in _err(lib)
+    assert call(qs, ks, q, ks + 0x3f0) == 1 and "overlaps" in _err(lib)
+    assert call(qs, ks, ks, k) == 1 and "overlaps" in _err(lib)
+    # in place with a different stride for the source and the output
+    wide = (ctypes.c_int64 * 2)(256, 128)
+    assert call(qs, ks, qs, k, src_strides=wide) == 1 and "stride" in _err(lib)
+    # work-list arguments: all or none
+    assert call(qs, ks, q, k, lst=(FAKE + 0x4000, 1, 4, 64, None, 1, FAKE + 0x5000, None)) == 1
+    assert call(qs, ks, q, k, lst=(None, 1, 4, 64, FAKE + 0x4000, 1, None, None)) == 1
+    # nothing to do: no tokens, or in place with neither norm nor rotary
+    assert call(qs, ks, q, k, T=0) == 0
+    assert call(qs, ks, qs, ks, pos=None) == 0
+
+
 def test_worklist_argument_errors(lib):
     f = lib.vit_varlen_worklist
     meta = FAKE + 0x40

@@ -44,28 +44,36 @@ def test_fp32_kernel_is_never_reported_as_hbm_bound():
 
 
 def _counter_csv(path, counter, rows):
+    """rows: (kernel name, value), in dispatch order; written to the file in
+    reverse, so that the reader has to sort them by dispatch id."""
     with open(path, "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name",
-                                          "Counter_Value"])
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size",
+                                          "Counter_Name", "Counter_Value"])
         w.writeheader()
-        for name, value in rows:
-            w.writerow({"Kernel_Name": name, "Grid_Size": 256, "Counter_Name": counter,
-                        "Counter_Value": value})
+        for i, (name, value) in reversed(list(enumerate(rows))):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Grid_Size": 256,
+                        "Counter_Name": counter, "Counter_Value": value})
 
 
 def test_pmc_summary_scales_each_counter_by_the_calibration_copy(tmp_path):
     # The copy of 64 MiB reads FETCH_SIZE = 32768 KiB (factor 2) and
-    # WRITE_SIZE = 65536 KiB (factor 1); two attention dispatches average
-    # 1000 KiB fetched and 300 KiB written.
+    # WRITE_SIZE = 65536 KiB (factor 1); the two timed attention dispatches
+    # (ordinals 1 and 2 of the step's attention kernel) average 1000 KiB
+    # fetched and 300 KiB written.  The warm-up dispatch before them, the
+    # side-loop dispatch after them and another attention kernel's dispatch
+    # are left out.
     fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
     attn = "void vit::attn_bf16_kernel<Cfg<80>>(...)"
-    _counter_csv(fetch, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 32768.0), (attn, 900.0),
-                                       (attn, 1100.0), ("prepass_kernel", 5.0)])
-    _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 65536.0), (attn, 300.0),
-                                       (attn, 300.0)])
+    other = "void vit::attn_bf16_kernel<Cfg<128>>(...)"
+    _counter_csv(fetch, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 32768.0), ("prepass_kernel", 5.0),
+                                       (attn, 7000.0), ("prepass_kernel", 5.0), (attn, 900.0),
+                                       ("prepass_kernel", 5.0), (attn, 1100.0), (attn, 9000.0),
+                                       (other, 8000.0)])
+    _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 65536.0), (attn, 700.0),
+                                       (attn, 300.0), (attn, 300.0), (attn, 900.0)])
     meta = tmp_path / "meta.json"
     meta.write_text(json.dumps({"copy_mib": 64, "workload": "w", "kernel_source_sha": "x",
-                                "algorithmic_bytes": 123}))
+                                "algorithmic_bytes": 123, "timed_dispatches": [1, 2]}))
     out = tmp_path / "traffic.json"
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-pmc",
                         str(fetch), str(write), "--calibration-meta", str(meta),
@@ -75,5 +83,5 @@ def test_pmc_summary_scales_each_counter_by_the_calibration_copy(tmp_path):
     assert res["fetch_bytes_per_launch"] == 1000 * 2 * 1024
     assert res["write_bytes_per_launch"] == 300 * 1 * 1024
     assert res["bytes_per_launch"] == (2000 + 300) * 1024
-    assert res["dispatches"] == {"FETCH_SIZE": 2, "WRITE_SIZE": 2}
+    assert res["dispatches"]["FETCH_SIZE"] == 2 and res["dispatches"]["WRITE_SIZE"] == 2
     assert res["algorithmic_bytes_per_launch"] == 123

@@ -36,6 +36,8 @@ SIGNATURES = {
     "vit_qk_norm_rope_ex": (_I, [_P, _P, _I64, _I, _I, _I, _P, _F, _P, _P, _F, _I, _P, _P]),
     "vit_qk_norm_rope_worklist": (_I, [_P, _P, _I64, _I, _I, _I, _P, _F, _P, _P, _F, _I, _P,
                                        _P, _I, _I, _I, _P, _I64, _P, _P]),
+    "vit_qk_norm_rope_into": (_I, [_P, _P, _P, _P, _P, _I64, _I, _I, _I, _P, _F, _P, _P, _F, _I,
+                                   _P, _P, _I, _I, _I, _P, _I64, _P, _P]),
     "vit_varlen_attn": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P]),
     "vit_varlen_attn_f32": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P]),
     "vit_attn_block_m": (_I, [_I, _I, _I]),

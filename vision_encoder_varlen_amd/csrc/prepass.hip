@@ -1,4 +1,5 @@
-// Fused Q/K RMSNorm + 2D rotary embedding, in place, fp32 arithmetic.
+// Fused Q/K RMSNorm + 2D rotary embedding, fp32 arithmetic, in place or from
+// separate source rows into the output rows.
 //
 // Norm: vLLM page vllm.models.dots3_note.nvidia.vision_attention, _RMSNorm
 // (mean of squares over the head dim, fp32 reduce, rsqrt, times a [D] weight
@@ -21,7 +22,8 @@
 //     partners m+D/2.., so the rotation is lane-local and only the sum of
 //     squares crosses lanes (an xor shuffle when G is a power of two).  E = 8
 //     for bf16 rows (16-byte accesses; a D = 80 row takes 5 lanes, so a wave
-//     holds 12 rows), else 4.  Every row is read and written exactly once.  A
+//     holds 12 rows), else 4.  Every row is read and written exactly once
+//     (the source row, then the output row; the same row in place).  A
 //     lane issues the four loads of its row (q and k, both halves) before any
 //     arithmetic, and token groups are small (about two rows per lane), so
 //     many workgroups keep enough loads in flight to approach HBM bandwidth.
@@ -103,11 +105,14 @@ __device__ __forceinline__ float row_sum(float v, int G, int base) {
   return t;
 }
 
+// Each lane loads all of its row elements before it stores any, and no
+// other lane touches that row, so a source row may be its own output row.
 template <typename T, int E>
 __global__ __launch_bounds__(kThreads) void prepass_kernel(
-    T* __restrict__ q, T* __restrict__ k, long long T_tok, int H, int D, int G, int tok_per_grp,
+    const T* qi, const T* ki, T* q, T* k, long long T_tok, int H, int D, int G, int tok_per_grp,
     const int32_t* __restrict__ pos, Freqs freqs, const float* __restrict__ wq,
-    const float* __restrict__ wk, float eps, WorklistJob job, int qs, int ks, int rope_mode) {
+    const float* __restrict__ wk, float eps, WorklistJob job, int qsi, int ksi, int qs, int ks,
+    int rope_mode) {
   extern __shared__ float2 cs[];  // [tok_per_grp][D/2] (cos, sin)
   __shared__ int s_wave[kThreads / 64];
   // With a work-list job workgroup 0 (dispatched first) builds the list,
@@ -180,16 +185,18 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
       const int h = row - tl * H;
       const size_t qbase = size_t(t0 + tl) * qs + size_t(h) * D;
       const size_t kbase = size_t(t0 + tl) * ks + size_t(h) * D;
+      const size_t qibase = size_t(t0 + tl) * qsi + size_t(h) * D;
+      const size_t kibase = size_t(t0 + tl) * ksi + size_t(h) * D;
       // Both tensors' loads are issued before any arithmetic, so each lane
       // keeps four independent loads in flight.
       float a[2][E] = {}, b[2][E] = {};
       if (row_ok) {
         if (has_q) {
-          loadE<E>(q + qbase + m0, a[0]);
-          loadE<E>(q + qbase + m0 + half_d, b[0]);
+          loadE<E>(qi + qibase + m0, a[0]);
+          loadE<E>(qi + qibase + m0 + half_d, b[0]);
         }
-        loadE<E>(k + kbase + m0, a[1]);
-        loadE<E>(k + kbase + m0 + half_d, b[1]);
+        loadE<E>(ki + kibase + m0, a[1]);
+        loadE<E>(ki + kibase + m0 + half_d, b[1]);
       }
       if (norm) {
         float ss[2];
@@ -261,16 +268,19 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
 
 }  // namespace
 
-hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
+hipError_t launch_prepass(const PrepassIO& io, int64_t T, int H, int D, int dtype,
                           const int32_t* pos, const double* inv_freq_host, const float* wq,
                           const float* wk, float eps, hipStream_t stream, hipEvent_t e0,
-                          hipEvent_t e1, const WorklistJob* job, int q_stride, int k_stride,
-                          int rope_mode) {
-  const int qs = q_stride > 0 ? q_stride : H * D;
-  const int ks = k_stride > 0 ? k_stride : H * D;
+                          hipEvent_t e1, const WorklistJob* job, int rope_mode) {
+  const int qs = io.q_stride > 0 ? io.q_stride : H * D;
+  const int ks = io.k_stride > 0 ? io.k_stride : H * D;
+  const int qsi = io.q_src_stride > 0 ? io.q_src_stride : H * D;
+  const int ksi = io.k_src_stride > 0 ? io.k_src_stride : H * D;
   WorklistJob jb{};
   if (job != nullptr) jb = *job;
-  const bool prepass_work = T > 0 && (pos != nullptr || wk != nullptr);
+  // Out of place, rows are copied even with neither norm nor rotary.
+  const bool in_place = io.q_src == io.q && io.k_src == io.k && qsi == qs && ksi == ks;
+  const bool prepass_work = T > 0 && (pos != nullptr || wk != nullptr || !in_place);
   if (!prepass_work) {
     if (jb.cu == nullptr) return hipSuccess;
     return launch_worklist(jb.cu, jb.N, jb.max_seqlen, jb.block_m, jb.items, jb.cap, jb.meta,
@@ -321,18 +331,25 @@ hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
       if (wl_lds > lds) lds = wl_lds;
     }
   }
-  if (dtype == 1 && E == 8) {
-    hipExtLaunchKernelGGL(prepass_kernel<u16, 8>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
-                          e0, e1, 0, static_cast<u16*>(q), static_cast<u16*>(k), (long long)T, H, D,
-                          G, tok_per_grp, pos, fr, wq, wk, eps, jb, qs, ks, rope_mode);
-  } else if (dtype == 1) {
-    hipExtLaunchKernelGGL(prepass_kernel<u16, 4>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
-                          e0, e1, 0, static_cast<u16*>(q), static_cast<u16*>(k), (long long)T, H, D,
-                          G, tok_per_grp, pos, fr, wq, wk, eps, jb, qs, ks, rope_mode);
+  if (dtype == 1) {
+    const u16* qi = static_cast<const u16*>(io.q_src);
+    const u16* ki = static_cast<const u16*>(io.k_src);
+    u16* q = static_cast<u16*>(io.q);
+    u16* k = static_cast<u16*>(io.k);
+    if (E == 8)
+      hipExtLaunchKernelGGL(prepass_kernel<u16, 8>, dim3(unsigned(grid)), dim3(kThreads), lds,
+                            stream, e0, e1, 0, qi, ki, q, k, (long long)T, H, D, G, tok_per_grp,
+                            pos, fr, wq, wk, eps, jb, qsi, ksi, qs, ks, rope_mode);
+    else
+      hipExtLaunchKernelGGL(prepass_kernel<u16, 4>, dim3(unsigned(grid)), dim3(kThreads), lds,
+                            stream, e0, e1, 0, qi, ki, q, k, (long long)T, H, D, G, tok_per_grp,
+                            pos, fr, wq, wk, eps, jb, qsi, ksi, qs, ks, rope_mode);
   } else {
-    hipExtLaunchKernelGGL(prepass_kernel<float, 4>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
-                          e0, e1, 0, static_cast<float*>(q), static_cast<float*>(k), (long long)T, H,
-                          D, G, tok_per_grp, pos, fr, wq, wk, eps, jb, qs, ks, rope_mode);
+    hipExtLaunchKernelGGL(prepass_kernel<float, 4>, dim3(unsigned(grid)), dim3(kThreads), lds,
+                          stream, e0, e1, 0, static_cast<const float*>(io.q_src),
+                          static_cast<const float*>(io.k_src), static_cast<float*>(io.q),
+                          static_cast<float*>(io.k), (long long)T, H, D, G, tok_per_grp, pos, fr,
+                          wq, wk, eps, jb, qsi, ksi, qs, ks, rope_mode);
   }
   return hipGetLastError();
 }

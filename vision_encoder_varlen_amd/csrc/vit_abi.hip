@@ -347,14 +347,70 @@ int check_worklist_args(const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
   return VIT_OK;
 }
 
-// Arguments already checked.  job: a work-list to build in the same launch,
-// or null.
-int launch_prepass_job(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
-                       int dtype, const int32_t* pos, float theta, const float* q_weight,
-                       const float* k_weight, float eps, int rope_mode,
-                       const vit::WorklistJob* job, const vit::TokenStrides& ts,
-                       hipStream_t stream, const TimingHook& t) {
-  const bool prepass_work = total_tokens > 0 && (pos != nullptr || k_weight != nullptr);
+// [first, last) byte range of a [T, H, D] tensor with `stride` elements per
+// token.
+struct ByteRange {
+  uintptr_t first, last;
+};
+ByteRange rows_range(const void* p, int64_t T, int64_t stride, int H, int D, int elt) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  if (p == nullptr || T == 0) return ByteRange{a, a};
+  return ByteRange{a, a + uintptr_t(((T - 1) * stride + int64_t(H) * D) * elt)};
+}
+bool overlap(ByteRange x, ByteRange y) {
+  return x.first < x.last && y.first < y.last && x.first < y.last && y.first < x.last;
+}
+
+// The pre-pass from q_src / k_src into q / k.  Each output either is its own
+// source with the same stride (in place: a lane reads its row before it
+// writes it) or shares no byte with either source; anything else could let
+// one lane's stores land on rows another lane has still to read.  job: a
+// work-list to build in the same launch, or null.
+int prepass_common(const void* q_src, const void* k_src, const int64_t* src_strides, void* q,
+                   void* k, int64_t total_tokens, int num_heads, int head_dim, int dtype,
+                   const int32_t* pos, float theta, const float* q_weight, const float* k_weight,
+                   float eps, int rope_mode, const int64_t* strides, const vit::WorklistJob* job,
+                   hipStream_t stream, const TimingHook& t) {
+  int rc = check_prepass_args(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta,
+                              q_weight, k_weight, eps, rope_mode);
+  if (rc != VIT_OK) return rc;
+  if (!k_src) return fail(VIT_ERR_INVALID_ARG, "null k_src");
+  if ((q_src == nullptr) != (q == nullptr))
+    return fail(VIT_ERR_INVALID_ARG, "q_src and q must both be given or both be null");
+  if (!aligned16(q_src) || !aligned16(k_src))
+    return fail(VIT_ERR_INVALID_ARG, "q_src and k_src must be 16-byte aligned");
+  vit::TokenStrides ts{}, tsi{};
+  rc = make_strides(strides, 2, num_heads, head_dim, dtype, &ts);
+  if (rc != VIT_OK) return rc;
+  rc = make_strides(src_strides, 2, num_heads, head_dim, dtype, &tsi);
+  if (rc != VIT_OK) return rc;
+  const int elt = dtype == VIT_BF16 ? 2 : 4;
+  const ByteRange src[2] = {rows_range(q_src, total_tokens, tsi.q, num_heads, head_dim, elt),
+                            rows_range(k_src, total_tokens, tsi.k, num_heads, head_dim, elt)};
+  const void* outs[2] = {q, k};
+  const void* srcs[2] = {q_src, k_src};
+  const int out_stride[2] = {ts.q, ts.k};
+  const int src_stride[2] = {tsi.q, tsi.k};
+  for (int i = 0; i < 2; ++i) {
+    if (outs[i] == nullptr) continue;
+    if (outs[i] == srcs[i]) {
+      if (out_stride[i] != src_stride[i])
+        return fail(VIT_ERR_INVALID_ARG, "%s is updated in place but its two strides differ",
+                    i == 0 ? "q" : "k");
+      // In place, q and k may interleave (views of one packed QKV buffer):
+      // their rows are distinct, which the check q != k covers as before.
+      continue;
+    }
+    const ByteRange r = rows_range(outs[i], total_tokens, out_stride[i], num_heads, head_dim, elt);
+    if (overlap(r, src[0]) || overlap(r, src[1]))
+      return fail(VIT_ERR_INVALID_ARG,
+                  "%s overlaps q_src or k_src (an output is either its own source, in place, or "
+                  "disjoint from both sources)", i == 0 ? "q" : "k");
+  }
+  const vit::PrepassIO io{q_src, k_src, q, k, tsi.q, tsi.k, ts.q, ts.k};
+  const bool in_place = q_src == q && k_src == k;
+  const bool prepass_work =
+      total_tokens > 0 && (pos != nullptr || k_weight != nullptr || !in_place);
   if (!prepass_work && job == nullptr) {
     const hipError_t e = record_empty(t, stream);
     return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
@@ -363,9 +419,9 @@ int launch_prepass_job(void* q, void* k, int64_t total_tokens, int num_heads, in
   double inv_freq[64];
   const int F = head_dim / 4;
   for (int j = 0; j < F; ++j) inv_freq[j] = std::pow(double(theta), -2.0 * j / (head_dim / 2.0));
-  hipError_t e = vit::launch_prepass(q, k, total_tokens, num_heads, head_dim, dtype, pos, inv_freq,
-                                     q_weight, k_weight, eps, stream, t.start, t.stop, job, ts.q,
-                                     ts.k, rope_mode);
+  hipError_t e = vit::launch_prepass(io, total_tokens, num_heads, head_dim, dtype, pos, inv_freq,
+                                     q_weight, k_weight, eps, stream, t.start, t.stop, job,
+                                     rope_mode);
   if (e != hipSuccess) return hip_fail(e, job ? "pre-pass + work-list launch" : "pre-pass launch");
   return ok();
 }
@@ -394,14 +450,8 @@ int vit_qk_norm_rope_ex(void* q, void* k, int64_t total_tokens, int num_heads, i
                         const float* k_weight, float eps, int rope_mode, const int64_t* strides,
                         hipStream_t stream) {
   const TimingHook t = take_timing();
-  int rc = check_prepass_args(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta,
-                              q_weight, k_weight, eps, rope_mode);
-  if (rc != VIT_OK) return rc;
-  vit::TokenStrides ts{};
-  rc = make_strides(strides, 2, num_heads, head_dim, dtype, &ts);
-  if (rc != VIT_OK) return rc;
-  return launch_prepass_job(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta, q_weight,
-                            k_weight, eps, rope_mode, nullptr, ts, stream, t);
+  return prepass_common(q, k, strides, q, k, total_tokens, num_heads, head_dim, dtype, pos, theta,
+                        q_weight, k_weight, eps, rope_mode, strides, nullptr, stream, t);
 }
 
 int vit_qk_norm_rope_worklist(void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
@@ -410,18 +460,28 @@ int vit_qk_norm_rope_worklist(void* q, void* k, int64_t total_tokens, int num_he
                               const int64_t* strides, const int32_t* cu_seqlens, int num_seqs,
                               int max_seqlen, int block_m, int32_t* items, int64_t cap,
                               int32_t* meta, hipStream_t stream) {
+  return vit_qk_norm_rope_into(q, k, strides, q, k, total_tokens, num_heads, head_dim, dtype, pos,
+                               theta, q_weight, k_weight, eps, rope_mode, strides, cu_seqlens,
+                               num_seqs, max_seqlen, block_m, items, cap, meta, stream);
+}
+
+int vit_qk_norm_rope_into(const void* q_src, const void* k_src, const int64_t* src_strides,
+                          void* q, void* k, int64_t total_tokens, int num_heads, int head_dim,
+                          int dtype, const int32_t* pos, float theta, const float* q_weight,
+                          const float* k_weight, float eps, int rope_mode, const int64_t* strides,
+                          const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int block_m,
+                          int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream) {
   const TimingHook t = take_timing();
-  int rc = check_prepass_args(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta, q_weight,
-                              k_weight, eps, rope_mode);
-  if (rc != VIT_OK) return rc;
-  vit::TokenStrides ts{};
-  rc = make_strides(strides, 2, num_heads, head_dim, dtype, &ts);
-  if (rc != VIT_OK) return rc;
-  rc = check_worklist_args(cu_seqlens, num_seqs, max_seqlen, block_m, items, cap, meta);
-  if (rc != VIT_OK) return rc;
-  const vit::WorklistJob job{cu_seqlens, num_seqs, 0, max_seqlen, block_m, items, cap, meta};
-  return launch_prepass_job(q, k, total_tokens, num_heads, head_dim, dtype, pos, theta, q_weight,
-                            k_weight, eps, rope_mode, &job, ts, stream, t);
+  const bool want_list = cu_seqlens != nullptr || items != nullptr || meta != nullptr;
+  vit::WorklistJob job{};
+  if (want_list) {
+    const int rc = check_worklist_args(cu_seqlens, num_seqs, max_seqlen, block_m, items, cap, meta);
+    if (rc != VIT_OK) return rc;
+    job = vit::WorklistJob{cu_seqlens, num_seqs, 0, max_seqlen, block_m, items, cap, meta};
+  }
+  return prepass_common(q_src, k_src, src_strides, q, k, total_tokens, num_heads, head_dim, dtype,
+                        pos, theta, q_weight, k_weight, eps, rope_mode, strides,
+                        want_list ? &job : nullptr, stream, t);
 }
 
 int vit_varlen_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,

@@ -117,17 +117,30 @@ struct WorklistJob {
 // larger lists get a launch of their own.
 constexpr size_t kFusedWorklistMaxLds = 24 * 1024;
 
+// Rows the pre-pass reads (q_src, k_src) and writes (q, k), with their token
+// strides in elements (0 = H * D).  Sources equal to the outputs, with the
+// same strides, are the in-place form; q_src and q are both null when only k
+// is processed.
+struct PrepassIO {
+  const void* q_src;
+  const void* k_src;
+  void* q;
+  void* k;
+  int q_src_stride;
+  int k_src_stride;
+  int q_stride;
+  int k_stride;
+};
+
 // Pre-pass: inv_freq_host holds the D/4 rotary inverse frequencies in double
-// (may be null when pos is null).  dtype: 0 = fp32, 1 = bf16.  q_stride /
-// k_stride: elements per token (0 = H * D).  With a job,
+// (may be null when pos is null).  dtype: 0 = fp32, 1 = bf16.  With a job,
 // the work-list is built by one more workgroup of the same launch (the two
 // are independent).
-hipError_t launch_prepass(void* q, void* k, int64_t T, int H, int D, int dtype,
+hipError_t launch_prepass(const PrepassIO& io, int64_t T, int H, int D, int dtype,
                           const int32_t* pos, const double* inv_freq_host,
                           const float* wq, const float* wk, float eps, hipStream_t stream,
-                          hipEvent_t ev_start, hipEvent_t ev_stop,
-                          const WorklistJob* job = nullptr, int q_stride = 0, int k_stride = 0,
-                          int rope_mode = 0);
+                          hipEvent_t ev_start, hipEvent_t ev_stop, const WorklistJob* job,
+                          int rope_mode);
 
 hipError_t launch_worklist(const int32_t* cu, int N, int max_seqlen, int block_m,
                            int32_t* items, int64_t cap, int32_t* meta, hipStream_t stream,

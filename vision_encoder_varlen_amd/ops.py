@@ -121,6 +121,42 @@ def qk_norm_rope_worklist_(q: torch.Tensor, k: torch.Tensor, pos: Optional[torch
     return plan
 
 
+def qk_norm_rope_into(q_src: Optional[torch.Tensor], k_src: torch.Tensor,
+                      q: Optional[torch.Tensor], k: torch.Tensor, pos: Optional[torch.Tensor],
+                      theta: float = 10000.0, q_weight: Optional[torch.Tensor] = None,
+                      k_weight: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                      rope_mode: str = "neox", plan: Optional["Plan"] = None,
+                      cu_seqlens: Optional[torch.Tensor] = None) -> None:
+    """Q/K RMSNorm then 2D rotary from ``q_src`` / ``k_src`` (left unchanged)
+    into ``q`` / ``k``; with ``plan`` and ``cu_seqlens`` the plan's work-list
+    is rebuilt in the same launch.  An output is either its own source (in
+    place) or shares no memory with the sources."""
+    _prepass_checks(q, k, pos, q_weight, k_weight)
+    if (q_src is None) != (q is None):
+        raise ValueError("q_src and q must both be given or both be None")
+    if q_src is not None:
+        _need_cuda("q_src", q_src, q.dtype, token_strided=True)
+        if q_src.shape != q.shape:
+            raise ValueError("q_src must have the shape of q")
+    _need_cuda("k_src", k_src, k.dtype, token_strided=True)
+    if k_src.shape != k.shape:
+        raise ValueError("k_src must have the shape of k")
+    if (plan is None) != (cu_seqlens is None):
+        raise ValueError("give plan and cu_seqlens together")
+    if plan is not None:
+        _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
+        if cu_seqlens.numel() - 1 != plan.num_seqs:
+            raise ValueError("cu_seqlens does not match the plan")
+    T, H, D = k.shape
+    lst = (None, 0, 0, 0, None, 0, None) if plan is None else (
+        cu_seqlens.data_ptr(), plan.num_seqs, plan.max_seqlen, plan.block_m, plan.items.data_ptr(),
+        plan.cap, plan.meta.data_ptr())
+    _lib.check(_lib.load().vit_qk_norm_rope_into(
+        _ptr(q_src), k_src.data_ptr(), _strides_qk(q_src, k_src), _ptr(q), k.data_ptr(), T, H, D,
+        dtype_code(k.dtype), _ptr(pos), float(theta), _ptr(q_weight), _ptr(k_weight), float(eps),
+        _rope_mode(rope_mode), _strides_qk(q, k), *lst, _stream(k)))
+
+
 def _attn_checks(q, k, v, cu_seqlens):
     _need_cuda("q", q, token_strided=True)
     for name, t in (("k", k), ("v", v)):

@@ -35,13 +35,24 @@ def attn_errors(got: np.ndarray, want: np.ndarray):
     return max_abs, rel_l2
 
 
-def assert_attn_close(got: np.ndarray, want: np.ndarray, dtype: str, what: str = ""):
+def assert_attn_close(got: np.ndarray, want: np.ndarray, dtype: str, what: str = "",
+                      peaked: bool = False):
+    """peaked: rows that may return nearly single V rows (causal rows near a
+    segment's start see only a few keys), whose magnitude can pass 4; there
+    the bf16 weights P and the bf16 store each move an output by up to 2^-9
+    of its size, so a bf16 element may differ by 1.5e-2 + 2^-8 |exact|."""
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     max_abs, rel_l2 = attn_errors(got, want)
     if dtype == "f32":
         assert max_abs <= F32_MAX_ABS, f"{what}: fp32 max-abs {max_abs:.3e} > {F32_MAX_ABS}"
     else:
-        assert max_abs <= BF16_MAX_ABS, f"{what}: bf16 max-abs {max_abs:.3e} > {BF16_MAX_ABS}"
+        if peaked:
+            err = np.abs(got - want)
+            tol = BF16_MAX_ABS + 2.0 ** -8 * np.abs(want)
+            worst = float((err / tol).max()) if err.size else 0.0
+            assert worst <= 1.0, f"{what}: bf16 error {worst:.3f} of the magnitude-scaled bound"
+        else:
+            assert max_abs <= BF16_MAX_ABS, f"{what}: bf16 max-abs {max_abs:.3e} > {BF16_MAX_ABS}"
         assert rel_l2 <= BF16_REL_L2, f"{what}: bf16 rel-L2 {rel_l2:.3e} > {BF16_REL_L2}"
     return max_abs, rel_l2
 

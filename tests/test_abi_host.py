@@ -50,7 +50,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_block_m_and_capacity(lib):
-    assert lib.vit_attn_block_m(16, 80, _lib.VIT_BF16) == 128
+    assert lib.vit_attn_block_m(16, 80, _lib.VIT_BF16) == 256
+    assert lib.vit_attn_block_m(16, 128, _lib.VIT_BF16) == 128
     assert lib.vit_attn_block_m(2, 32, _lib.VIT_F32) == 32
     assert lib.vit_attn_block_m(16, 72, _lib.VIT_BF16) == -_lib.VIT_ERR_UNSUPPORTED
     assert lib.vit_attn_block_m(0, 64, _lib.VIT_BF16) == -_lib.VIT_ERR_INVALID_ARG

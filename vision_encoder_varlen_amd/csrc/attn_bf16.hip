@@ -11,8 +11,9 @@
 // holding its last row.
 //
 // Design (one workgroup = WAVES waves; each wave owns 32*QB query rows of
-// one head; two workgroups share a CU so one's softmax overlaps the other's
-// MFMA):
+// one head; two waves share each SIMD so one's softmax overlaps the other's
+// MFMA -- two 4-wave workgroups per CU, or one 8-wave workgroup, whose waves
+// then share one K/V ring: half the global -> LDS copies per CU):
 //  * Q fragments stay in VGPRs for the whole key loop.
 //  * K and V tiles of BN keys are copied global -> LDS by the buffer unit
 //    itself (buffer_load_dwordx4 ... lds) into a ring of STAGES buffers, issued
@@ -93,6 +94,7 @@ struct Cfg {
   static constexpr int STAGES = STAGES_;                // LDS ring depth
   static constexpr int OCC = OCC_;                      // waves per SIMD the kernel is built for
   static constexpr int THREADS = 64 * WAVES;
+  static constexpr int WG_PER_CU = 4 * OCC / WAVES;     // resident workgroups per CU (4 SIMDs)
   static constexpr int BM = 32 * QB * WAVES;            // query rows per workgroup
   static constexpr int KB = BN / 32;                    // 32-key blocks per tile
   static constexpr int KSTEPS = D / 16;                 // 16-wide contraction steps of Q K^T
@@ -119,7 +121,8 @@ struct Cfg {
   static_assert(BN <= kMaxKeyTile, "key tile exceeds the padding the segment limit allows for");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
   static_assert(NI_HI * (STAGES - 2) <= 63, "vmcnt range");
-  static_assert(LDS_BYTES * OCC <= 160 * 1024, "LDS budget");
+  static_assert((4 * OCC) % WAVES == 0 && WG_PER_CU >= 1, "whole workgroups per CU");
+  static_assert(LDS_BYTES * WG_PER_CU <= 160 * 1024, "LDS budget");
 };
 
 // The value lane l ^ 32 holds (v_permlane32_swap: a VALU exchange of the two
@@ -210,10 +213,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
   // Per-lane byte offsets of this wave's copy instructions relative to the
   // tile's first key.  Instruction i = wave + WAVES*j (K units first, then V
   // units); lanes that fall on row padding get an offset past num_records and
-  // write zeros.
+  // write zeros.  With kSumByMfma the head-dim padding units of the V rows
+  // are not copied at all (cp_skip): they hold a constant 1 in dim D, written
+  // once below, so row D of V^T is all ones without any per-tile work.
   const bool wave_hi = wave < C::NT % C::WAVES || C::NT % C::WAVES == 0;
   unsigned cp_off[NI];
   bool cp_is_k[NI];
+  bool cp_skip[NI];
   unsigned cp_lds[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
@@ -228,7 +234,24 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     cp_off[j] = data ? (unsigned(key) * unsigned(is_k ? ts.k : ts.v) + unsigned(col) * 8u) * 2u
                      : kPadOffset;
     cp_is_k[j] = is_k;
+    cp_skip[j] = kSumByMfma && !is_k && row < BN && col >= C::DU;
     cp_lds[j] = unsigned((is_k ? i * 64 : C::KREG + (i - C::NK) * 64) * 16);
+  }
+  if constexpr (kSumByMfma) {
+    // V row padding of every ring stage: unit DU starts with bf16 1.0 (dim D),
+    // the rest are zero.  No copy writes these units (cp_skip), and the first
+    // tile's barrier orders these stores before any read.
+    static_assert(C::VSTR > C::DU && kOnesLane % 8 == 0, "dim D must open a padding unit");
+    constexpr int kPadUnits = C::VSTR - C::DU;
+    for (int i = tid; i < STAGES * BN * kPadUnits; i += C::THREADS) {
+      const int stage = i / (BN * kPadUnits);
+      const int r = (i / kPadUnits) % BN;
+      const int pu = i % kPadUnits;
+      u32x4_t val = u32x4_t{0u, 0u, 0u, 0u};
+      if (pu == 0) val.x = 0x3f80u;  // dims D, D+1 = (1.0, 0) in the low dword
+      *reinterpret_cast<u32x4_t*>(smem + (stage * C::STAGE_UNITS + C::KREG + r * C::VSTR + C::DU + pu) * 8) =
+          val;
+    }
   }
 
   // Q-side pre-pass (when asked for): each unit's Q fragments are normalised
@@ -237,7 +260,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
   // hi + lo).
   __shared__ float s_qw[D];
   __shared__ float2 s_rev[kMaxQFreqs];
-  static_assert((C::LDS_BYTES + D * 4 + kMaxQFreqs * 8) * C::OCC <= 160 * 1024,
+  static_assert((C::LDS_BYTES + D * 4 + kMaxQFreqs * 8) * C::WG_PER_CU <= 160 * 1024,
                 "LDS budget with the pre-pass tables");
   const bool q_pending = qpre.pos != nullptr || qpre.weight != nullptr;
   if (q_pending) {
@@ -461,7 +484,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       const unsigned stage_lds = smem_base + unsigned((t % STAGES) * C::STAGE_UNITS * 16);
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        if (j < C::NI_LO || wave_hi)
+        if ((j < C::NI_LO || wave_hi) && !cp_skip[j])
           copy_to_lds(stage_lds + cp_lds[j], cp_off[j] + (cp_is_k[j] ? tile_off_k : tile_off_v),
                       cp_is_k[j] ? krs : vrs);
     };
@@ -532,17 +555,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
             }
       }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (kSumByMfma && MODE != kMaxOnly) {
-        // Head-dim row D of V^T (padding, zero in LDS) becomes all ones, so
-        // row D of O^T accumulates the row sums of P.
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int qh = 0; qh < 2; ++qh)
-              if (l32 == kOnesLane) vf[kb][s2][C::DB - 1][qh] = i16x4_t{0x3f80, 0x3f80, 0x3f80, 0x3f80};
-      }
+      // With kSumByMfma, head-dim row D of V^T is all ones in LDS, so row D of
+      // O^T accumulates the row sums of P.
 
       // S^T = K Q^T for every query block (each K fragment feeds QB MFMAs).
       f32x16_t sc[QB][KB];
@@ -719,12 +733,16 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const Schedul
   return hipGetLastError();
 }
 
-// Per head dim: (waves, keys per tile, ring depth, waves per SIMD).  Rows per
-// workgroup must equal bf16_block_m_const(D).
+// Per head dim: (waves, query blocks per wave, keys per tile, ring depth,
+// waves per SIMD).  Rows per workgroup must equal bf16_block_m_const(D).
+// D = 80 takes 8-wave workgroups: one K/V ring per CU instead of two halves
+// the copies into LDS, and the 4 x 1024-token batch runs 7% faster (31 us
+// instead of 33); at D = 128 the 256-row q-tiles lose more on the ragged
+// batch's short segments than the shared ring gains.
 template <int D> struct Choice;
 template <> struct Choice<32> { using C = Cfg<32, 4, 1, 64, 2, 2>; };
 template <> struct Choice<64> { using C = Cfg<64, 4, 1, 64, 2, 2>; };
-template <> struct Choice<80> { using C = Cfg<80, 4, 1, 64, 2, 2>; };
+template <> struct Choice<80> { using C = Cfg<80, 8, 1, 64, 2, 2>; };
 template <> struct Choice<96> { using C = Cfg<96, 4, 1, 64, 2, 2>; };
 template <> struct Choice<128> { using C = Cfg<128, 4, 1, 32, 2, 2>; };
 

@@ -63,8 +63,8 @@ struct Schedule {
 // that are recorded at its kernel's dispatch start and end (hipExtLaunchKernel).
 
 // Query rows per (segment, q-tile) work item.
-// bf16 MFMA kernel: 4 waves x 32 rows.
-constexpr int bf16_block_m_const(int /*head_dim*/) { return 128; }
+// bf16 MFMA kernel: 32 rows per wave, 8 waves at head dim 80, else 4.
+constexpr int bf16_block_m_const(int head_dim) { return head_dim == 80 ? 256 : 128; }
 constexpr int kBlockMF32 = 32;  // 1 wave, lane pairs share a row, fp32 kernel
 
 // Work-list builder limits: one workgroup sorts every segment in LDS.

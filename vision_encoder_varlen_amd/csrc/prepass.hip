@@ -58,12 +58,18 @@ __device__ __forceinline__ float bf16_to_f32(unsigned int bits16) {
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-// E consecutive elements <-> fp32 registers (one 8- or 16-byte access).
+// E consecutive elements: one 8- or 16-byte load kept as raw bits, unpacked
+// to fp32 only where the values are used, so the loads of a row are all in
+// flight before the first wait.
 template <int E>
-__device__ __forceinline__ void loadE(const float* p, float x[E]) {
+__device__ __forceinline__ u32x4_t loadRaw(const float* p) {
   static_assert(E == 4, "fp32 rows are handled 4 elements per access");
-  const float4 v = *reinterpret_cast<const float4*>(p);
-  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+template <int E>
+__device__ __forceinline__ void unpackE(const float*, const u32x4_t& v, float x[E]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(v[i]);
 }
 template <int E>
 __device__ __forceinline__ void storeE(float* p, const float x[E]) {
@@ -71,18 +77,26 @@ __device__ __forceinline__ void storeE(float* p, const float x[E]) {
   *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
 template <int E>
-__device__ __forceinline__ void loadE(const u16* p, float x[E]) {
-  if constexpr (E == 8) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+__device__ __forceinline__ u32x4_t loadRaw(const u16* p) {
+  if constexpr (E == 8) return *reinterpret_cast<const u32x4_t*>(p);
+  const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
+  return u32x4_t{v.x, v.y, 0u, 0u};
+}
+template <int E>
+__device__ __forceinline__ void unpackE(const u16*, const u32x4_t& v, float x[E]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = bf16_to_f32(v[i] & 0xffffu);
-      x[2 * i + 1] = bf16_to_f32(v[i] >> 16);
-    }
-  } else {
-    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
-    x[0] = bf16_to_f32(v.x & 0xffffu); x[1] = bf16_to_f32(v.x >> 16);
-    x[2] = bf16_to_f32(v.y & 0xffffu); x[3] = bf16_to_f32(v.y >> 16);
+  for (int i = 0; i < E / 2; ++i) {
+    x[2 * i] = bf16_to_f32(v[i] & 0xffffu);
+    x[2 * i + 1] = bf16_to_f32(v[i] >> 16);
+  }
+}
+// The norm weights of a lane's E dims (16-byte aligned fp32).
+template <int E>
+__device__ __forceinline__ void loadWeights(const float* p, float x[E]) {
+#pragma unroll
+  for (int i = 0; i < E / 4; ++i) {
+    const float4 v = *reinterpret_cast<const float4*>(p + 4 * i);
+    x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
   }
 }
 template <int E>
@@ -146,121 +160,173 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(
   // Norm weights of this lane's dims, the same for every row.
   float wa[2][E] = {}, wb[2][E] = {};
   if (norm && lane_active) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      wa[0][e] = has_q ? wq[m0 + e] : 0.f;
-      wb[0][e] = has_q ? wq[m0 + half_d + e] : 0.f;
-      wa[1][e] = wk[m0 + e];
-      wb[1][e] = wk[m0 + half_d + e];
+    if (has_q) {
+      loadWeights<E>(wq + m0, wa[0]);
+      loadWeights<E>(wq + m0 + half_d, wb[0]);
     }
+    loadWeights<E>(wk + m0, wa[1]);
+    loadWeights<E>(wk + m0 + half_d, wb[1]);
   }
+
+  // One pass of rows: the loads (issued before any arithmetic, both tensors,
+  // so each lane keeps four independent loads in flight), then norm, rotary
+  // and stores.
+  struct Rows {
+    u32x4_t ra[2], rb[2];  // raw loads: first and second half of q's and k's row
+    size_t qbase, kbase;
+    int tl;
+    bool row_ok;
+  };
+  // A lane without a row reads the group's row 0 and discards it, so no
+  // per-lane branch surrounds the loads.
+  auto load_rows = [&](long long t0, int ntok, int r0) {
+    Rows rw_;
+    const int row = r0 + row_in_pass;  // (token_local, head) row inside the group
+    rw_.row_ok = row < ntok * H && lane_active;
+    const int tl = row / H;
+    const int h = row - tl * H;
+    rw_.tl = tl;
+    rw_.qbase = size_t(t0 + tl) * qs + size_t(h) * D;
+    rw_.kbase = size_t(t0 + tl) * ks + size_t(h) * D;
+    const int ltl = rw_.row_ok ? tl : 0, lh = rw_.row_ok ? h : 0;
+    const size_t qibase = size_t(t0 + ltl) * qsi + size_t(lh) * D;
+    const size_t kibase = size_t(t0 + ltl) * ksi + size_t(lh) * D;
+    rw_.ra[0] = rw_.rb[0] = u32x4_t{0u, 0u, 0u, 0u};
+    if (has_q) {
+      rw_.ra[0] = loadRaw<E>(qi + qibase + m0);
+      rw_.rb[0] = loadRaw<E>(qi + qibase + m0 + half_d);
+    }
+    rw_.ra[1] = loadRaw<E>(ki + kibase + m0);
+    rw_.rb[1] = loadRaw<E>(ki + kibase + m0 + half_d);
+    return rw_;
+  };
+  auto finish_rows = [&](Rows& rw_) {
+    float a[2][E], b[2][E];
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      unpackE<E>(qi, rw_.ra[which], a[which]);
+      unpackE<E>(qi, rw_.rb[which], b[which]);
+    }
+    const bool row_ok = rw_.row_ok;
+    const int tl = rw_.tl;
+    const size_t qbase = rw_.qbase, kbase = rw_.kbase;
+    if (norm) {
+      float ss[2];
+#pragma unroll
+      for (int which = 0; which < 2; ++which) {
+        ss[which] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          ss[which] = fmaf(a[which][e], a[which][e], fmaf(b[which][e], b[which][e], ss[which]));
+        ss[which] = row_sum(ss[which], G, rw * G);
+      }
+#pragma unroll
+      for (int which = 0; which < 2; ++which) {
+        const float rinv = rsqrtf(ss[which] * inv_d + eps);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          a[which][e] = a[which][e] * rinv * wa[which][e];
+          b[which][e] = b[which][e] * rinv * wb[which][e];
+        }
+      }
+    }
+    if (rope && row_ok && rope_mode == 0) {
+      // Rotate-half: element m of the first half pairs with m + D/2 and
+      // turns by angle m.
+      const float2* c = cs + tl * half_d + m0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float2 cse = c[e];
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+          const float ya = a[which][e] * cse.x - b[which][e] * cse.y;
+          const float yb = b[which][e] * cse.x + a[which][e] * cse.y;
+          a[which][e] = ya;
+          b[which][e] = yb;
+        }
+      }
+    } else if (rope && row_ok) {
+      // Complex form: elements (2j, 2j+1) are one complex number turned by
+      // angle j.  This lane's first-half dims hold pairs m0/2 .., its
+      // second-half dims pairs D/4 + m0/2 ..
+      const float2* ca = cs + tl * half_d + m0 / 2;
+      const float2* cb = ca + quarter_d;
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) {
+        const float2 c1 = ca[i], c2 = cb[i];
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+          const float a0 = a[which][2 * i], a1 = a[which][2 * i + 1];
+          a[which][2 * i] = a0 * c1.x - a1 * c1.y;
+          a[which][2 * i + 1] = a1 * c1.x + a0 * c1.y;
+          const float b0 = b[which][2 * i], b1 = b[which][2 * i + 1];
+          b[which][2 * i] = b0 * c2.x - b1 * c2.y;
+          b[which][2 * i + 1] = b1 * c2.x + b0 * c2.y;
+        }
+      }
+    }
+    if (row_ok) {
+      if (has_q) {
+        storeE<E>(q + qbase + m0, a[0]);
+        storeE<E>(q + qbase + m0 + half_d, b[0]);
+      }
+      storeE<E>(k + kbase + m0, a[1]);
+      storeE<E>(k + kbase + m0 + half_d, b[1]);
+    }
+  };
 
   for (long long t0 = (long long)pblock * tok_per_grp; t0 < T_tok;
        t0 += (long long)npre * tok_per_grp) {
     const int ntok = T_tok - t0 < tok_per_grp ? int(T_tok - t0) : tok_per_grp;
+    // The first pass of rows is loaded before the cos/sin table's inputs, so
+    // the two fetches overlap: the table waits once for both (loads complete
+    // in order), instead of its inputs' latency and then the rows' one after
+    // the other.
+    auto table_entry = [&](int i, int coord_i, float f_hi, float f_lo) {
+      const float coord = float(coord_i);
+      // angle = a_hi + a_lo exactly up to the rounding of a_lo: fmaf recovers
+      // the rounding error of coord * hi.
+      const float a_hi = coord * f_hi;
+      const float a_lo = fmaf(coord, f_hi, -a_hi) + coord * f_lo;
+      float sn, cn;
+      sincosf(a_hi, &sn, &cn);
+      // first-order correction for a_lo (|a_lo| <= 2^-23 |a_hi|; the neglected
+      // second-order term is below 2^-46 |a_hi|^2)
+      cs[i] = make_float2(fmaf(-sn, a_lo, cn), fmaf(cn, a_lo, sn));
+    };
+    // entry i: token i / (D/2), pair m = i mod (D/2); the row coordinate for
+    // m < D/4, the column for the rest, with frequency m mod D/4
+    auto entry_coord = [&](int i) {
+      const int tl = i / half_d;
+      const int m = i - tl * half_d;
+      return pos[2 * (t0 + tl) + (m < quarter_d ? 0 : 1)];
+    };
+    auto entry_freq = [&](int i) {
+      const int m = i % half_d;
+      return m < quarter_d ? m : m - quarter_d;
+    };
+    Rows first = load_rows(t0, ntok, 0);
+    const bool own_entry = rope && tid < ntok * half_d;
+    int c0 = 0;
+    float h0 = 0.f, l0 = 0.f;
+    if (rope) {  // uniform; a thread without an entry reads entry 0's inputs
+      const int ei = own_entry ? tid : 0;
+      c0 = entry_coord(ei);
+      h0 = freqs.hi[entry_freq(ei)];
+      l0 = freqs.lo[entry_freq(ei)];
+    }
     if (rope) {
-      for (int i = tid; i < ntok * half_d; i += kThreads) {
-        const int tl = i / half_d;
-        const int m = i - tl * half_d;
-        const long long t = t0 + tl;
-        const float coord = m < quarter_d ? float(pos[2 * t]) : float(pos[2 * t + 1]);
-        const int j = m < quarter_d ? m : m - quarter_d;
-        // angle = a_hi + a_lo exactly up to the rounding of a_lo: fmaf recovers
-        // the rounding error of coord * hi.
-        const float a_hi = coord * freqs.hi[j];
-        const float a_lo = fmaf(coord, freqs.hi[j], -a_hi) + coord * freqs.lo[j];
-        float sn, cn;
-        sincosf(a_hi, &sn, &cn);
-        // first-order correction for a_lo (|a_lo| <= 2^-23 |a_hi|; the neglected
-        // second-order term is below 2^-46 |a_hi|^2)
-        cs[i] = make_float2(fmaf(-sn, a_lo, cn), fmaf(cn, a_lo, sn));
+      if (own_entry) table_entry(tid, c0, h0, l0);
+      for (int i = tid + kThreads; i < ntok * half_d; i += kThreads) {
+        const int j = entry_freq(i);
+        table_entry(i, entry_coord(i), freqs.hi[j], freqs.lo[j]);
       }
       __syncthreads();
     }
-
-    for (int r0 = 0; r0 < ntok * H; r0 += rows_per_pass) {
-      const int row = r0 + row_in_pass;  // (token_local, head) row inside the group
-      const bool row_ok = row < ntok * H && lane_active;
-      const int tl = row / H;
-      const int h = row - tl * H;
-      const size_t qbase = size_t(t0 + tl) * qs + size_t(h) * D;
-      const size_t kbase = size_t(t0 + tl) * ks + size_t(h) * D;
-      const size_t qibase = size_t(t0 + tl) * qsi + size_t(h) * D;
-      const size_t kibase = size_t(t0 + tl) * ksi + size_t(h) * D;
-      // Both tensors' loads are issued before any arithmetic, so each lane
-      // keeps four independent loads in flight.
-      float a[2][E] = {}, b[2][E] = {};
-      if (row_ok) {
-        if (has_q) {
-          loadE<E>(qi + qibase + m0, a[0]);
-          loadE<E>(qi + qibase + m0 + half_d, b[0]);
-        }
-        loadE<E>(ki + kibase + m0, a[1]);
-        loadE<E>(ki + kibase + m0 + half_d, b[1]);
-      }
-      if (norm) {
-        float ss[2];
-#pragma unroll
-        for (int which = 0; which < 2; ++which) {
-          ss[which] = 0.f;
-#pragma unroll
-          for (int e = 0; e < E; ++e)
-            ss[which] = fmaf(a[which][e], a[which][e], fmaf(b[which][e], b[which][e], ss[which]));
-          ss[which] = row_sum(ss[which], G, rw * G);
-        }
-#pragma unroll
-        for (int which = 0; which < 2; ++which) {
-          const float rinv = rsqrtf(ss[which] * inv_d + eps);
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            a[which][e] = a[which][e] * rinv * wa[which][e];
-            b[which][e] = b[which][e] * rinv * wb[which][e];
-          }
-        }
-      }
-      if (rope && row_ok && rope_mode == 0) {
-        // Rotate-half: element m of the first half pairs with m + D/2 and
-        // turns by angle m.
-        const float2* c = cs + tl * half_d + m0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float2 cse = c[e];
-#pragma unroll
-          for (int which = 0; which < 2; ++which) {
-            const float ya = a[which][e] * cse.x - b[which][e] * cse.y;
-            const float yb = b[which][e] * cse.x + a[which][e] * cse.y;
-            a[which][e] = ya;
-            b[which][e] = yb;
-          }
-        }
-      } else if (rope && row_ok) {
-        // Complex form: elements (2j, 2j+1) are one complex number turned by
-        // angle j.  This lane's first-half dims hold pairs m0/2 .., its
-        // second-half dims pairs D/4 + m0/2 ..
-        const float2* ca = cs + tl * half_d + m0 / 2;
-        const float2* cb = ca + quarter_d;
-#pragma unroll
-        for (int i = 0; i < E / 2; ++i) {
-          const float2 c1 = ca[i], c2 = cb[i];
-#pragma unroll
-          for (int which = 0; which < 2; ++which) {
-            const float a0 = a[which][2 * i], a1 = a[which][2 * i + 1];
-            a[which][2 * i] = a0 * c1.x - a1 * c1.y;
-            a[which][2 * i + 1] = a1 * c1.x + a0 * c1.y;
-            const float b0 = b[which][2 * i], b1 = b[which][2 * i + 1];
-            b[which][2 * i] = b0 * c2.x - b1 * c2.y;
-            b[which][2 * i + 1] = b1 * c2.x + b0 * c2.y;
-          }
-        }
-      }
-      if (row_ok) {
-        if (has_q) {
-          storeE<E>(q + qbase + m0, a[0]);
-          storeE<E>(q + qbase + m0 + half_d, b[0]);
-        }
-        storeE<E>(k + kbase + m0, a[1]);
-        storeE<E>(k + kbase + m0 + half_d, b[1]);
-      }
+    finish_rows(first);
+    for (int r0 = rows_per_pass; r0 < ntok * H; r0 += rows_per_pass) {
+      Rows cur = load_rows(t0, ntok, r0);
+      finish_rows(cur);
     }
     if (rope) __syncthreads();  // cs is rewritten by the next token group
   }
@@ -331,25 +397,21 @@ hipError_t launch_prepass(const PrepassIO& io, int64_t T, int H, int D, int dtyp
       if (wl_lds > lds) lds = wl_lds;
     }
   }
+  auto launch = [&](auto kernel, const auto* qi, const auto* ki, auto* q, auto* k) {
+    hipExtLaunchKernelGGL(kernel, dim3(unsigned(grid)), dim3(kThreads), lds, stream, e0, e1, 0, qi,
+                          ki, q, k, (long long)T, H, D, G, tok_per_grp, pos, fr, wq, wk, eps, jb,
+                          qsi, ksi, qs, ks, rope_mode);
+  };
   if (dtype == 1) {
     const u16* qi = static_cast<const u16*>(io.q_src);
     const u16* ki = static_cast<const u16*>(io.k_src);
     u16* q = static_cast<u16*>(io.q);
     u16* k = static_cast<u16*>(io.k);
-    if (E == 8)
-      hipExtLaunchKernelGGL(prepass_kernel<u16, 8>, dim3(unsigned(grid)), dim3(kThreads), lds,
-                            stream, e0, e1, 0, qi, ki, q, k, (long long)T, H, D, G, tok_per_grp,
-                            pos, fr, wq, wk, eps, jb, qsi, ksi, qs, ks, rope_mode);
-    else
-      hipExtLaunchKernelGGL(prepass_kernel<u16, 4>, dim3(unsigned(grid)), dim3(kThreads), lds,
-                            stream, e0, e1, 0, qi, ki, q, k, (long long)T, H, D, G, tok_per_grp,
-                            pos, fr, wq, wk, eps, jb, qsi, ksi, qs, ks, rope_mode);
+    if (E == 8) launch(prepass_kernel<u16, 8>, qi, ki, q, k);
+    else launch(prepass_kernel<u16, 4>, qi, ki, q, k);
   } else {
-    hipExtLaunchKernelGGL(prepass_kernel<float, 4>, dim3(unsigned(grid)), dim3(kThreads), lds,
-                          stream, e0, e1, 0, static_cast<const float*>(io.q_src),
-                          static_cast<const float*>(io.k_src), static_cast<float*>(io.q),
-                          static_cast<float*>(io.k), (long long)T, H, D, G, tok_per_grp, pos, fr,
-                          wq, wk, eps, jb, qsi, ksi, qs, ks, rope_mode);
+    launch(prepass_kernel<float, 4>, static_cast<const float*>(io.q_src),
+           static_cast<const float*>(io.k_src), static_cast<float*>(io.q), static_cast<float*>(io.k));
   }
   return hipGetLastError();
 }

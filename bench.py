@@ -626,6 +626,7 @@ def mfma_ceiling(lib, torch, dev, stream):
     zeros.  The chip lowers its clock when operands toggle many bits, so the
     first figure is what any bf16 MFMA kernel can reach on such data."""
     from vision_encoder_varlen_amd import _lib
+    probe = _lib.load_probe()   # libvit_probe.so: measurement support, not the path
     nbytes = 4 << 20
     gen = torch.Generator(device="cpu").manual_seed(0)
     rnd = torch.randn(nbytes // 2, generator=gen).to(torch.bfloat16).to(dev)
@@ -640,15 +641,18 @@ def mfma_ceiling(lib, torch, dev, stream):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            _lib.check(lib.vit_probe_mfma(buf.data_ptr(), nbytes, blocks, iters, sink.data_ptr(),
-                                          stream.cuda_stream))
+            rc = probe.vit_probe_mfma(buf.data_ptr(), nbytes, blocks, iters, sink.data_ptr(),
+                                      stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"vit_probe_mfma: {probe.vit_probe_last_error().decode()}")
             e1.record(stream)
             e1.synchronize()
             times.append(e0.elapsed_time(e1))
         best = min(times[2:])  # the clock settles over the first launches
         out[name] = round(flops / (best * 1e-3) / 1e12, 1)
     out["unit"] = "TFLOP/s"
-    out["probe"] = "vit_probe_mfma: 512 workgroups x 4 waves, 4 independent 32x32x16 bf16 chains per wave"
+    out["probe"] = ("vit_probe_mfma (libvit_probe.so): 512 workgroups x 4 waves, 4 independent "
+                    "32x32x16 bf16 chains per wave")
     return out
 
 

@@ -395,22 +395,6 @@ int vit_varlen_attn_planned_qnorm_rope(
  */
 int vit_device_error(hipStream_t stream, int32_t* err, int reset);
 
-/*
- * Measurement support, not part of the attention path: the sustained bf16
- * MFMA rate on given operand data.  MI355X lowers its clock when MFMA
- * operands toggle many bits, so the rate depends on the data; timing this
- * probe with operands drawn like the inputs brackets what any bf16 MFMA
- * kernel can reach on them.  Runs `blocks` workgroups of 4 waves; each wave
- * issues 32 * iters v_mfma_f32_32x32x16_bf16 (4 * 32 * iters * 32768 FLOP per
- * workgroup) on operands read once.
- *  operands      device, 16-byte aligned, at least 4 MiB (64 slices of 256
- *                threads x 256 bytes, read as bf16).
- *  sink          device float [blocks * 256], written (keeps the work live).
- *  blocks        1 .. 65536; iters 1 .. 2^20.
- */
-int vit_probe_mfma(const void* operands, int64_t operand_bytes, int blocks, int iters, float* sink,
-                   hipStream_t stream);
-
 /* Message of the last failed call on this thread ("" if none). */
 const char* vit_last_error(void);
 

@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
     for required in ("vit_qk_norm_rope", "vit_varlen_attn", "vit_varlen_attn_f32",
                      "vit_varlen_worklist", "vit_varlen_attn_planned", "vit_attn_block_m",
                      "vit_worklist_capacity", "vit_device_error", "vit_last_error", "vit_release",
-                     "vit_time_next_kernel", "vit_probe_mfma", "vit_qk_norm_rope_worklist",
+                     "vit_time_next_kernel", "vit_qk_norm_rope_worklist",
                      "vit_varlen_attn_lse", "vit_varlen_attn_strided",
                      "vit_qk_norm_rope_strided", "vit_dense_batch_attn", "vit_qk_norm_rope_ex",
                      "vit_varlen_attn_ex", "vit_varlen_attn_planned_qnorm_rope"):
@@ -189,12 +189,22 @@ def test_timing_hook_needs_both_events_or_neither(lib):
     assert lib.vit_time_next_kernel(None, None) == _lib.VIT_OK
 
 
-def test_probe_argument_errors(lib):
-    f = lib.vit_probe_mfma
+def test_probe_library_is_separate_and_checks_arguments(lib):
+    """The MFMA-rate probe (measurement support) is in libvit_probe.so, which
+    exports what include/vit_probe.h declares; libvit.so does not export it."""
+    import re
+    assert not hasattr(lib, "vit_probe_mfma")
+    probe = _lib.load_probe()
+    header = open(os.path.join(ROOT, "include", "vit_probe.h")).read()
+    declared = set(re.findall(r"^(?:int|const char\*)\s+(vit_\w+)\(", header, re.M))
+    assert declared == {"vit_probe_mfma", "vit_probe_last_error"}
+    for name in declared:
+        assert hasattr(probe, name), name
+    f = probe.vit_probe_mfma
     big = 4 << 20
     assert f(None, big, 8, 10, FAKE, None) == _lib.VIT_ERR_INVALID_ARG
     assert f(FAKE, big - 16, 8, 10, FAKE, None) == _lib.VIT_ERR_INVALID_ARG
-    assert "bytes" in _err(lib)
+    assert "bytes" in probe.vit_probe_last_error().decode()
     assert f(FAKE, big, 0, 10, FAKE, None) == _lib.VIT_ERR_INVALID_ARG
     assert f(FAKE, big, 8, 0, FAKE, None) == _lib.VIT_ERR_INVALID_ARG
     assert f(FAKE + 8, big, 8, 10, FAKE, None) == _lib.VIT_ERR_INVALID_ARG

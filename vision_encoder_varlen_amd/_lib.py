@@ -54,7 +54,6 @@ SIGNATURES = {
     "vit_varlen_attn_lse": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P]),
     "vit_device_error": (_I, [_P, ctypes.POINTER(ctypes.c_int32), _I]),
     "vit_time_next_kernel": (_I, [_P, _P]),
-    "vit_probe_mfma": (_I, [_P, _I64, _I, _I, _P, _P]),
     "vit_last_error": (ctypes.c_char_p, []),
     "vit_release": (None, []),
 }
@@ -86,6 +85,31 @@ def load() -> ctypes.CDLL:
             fn.restype = res
             fn.argtypes = args
         _lib = lib
+        return lib
+
+
+# The MFMA-rate probe (measurement support) lives in a library of its own.
+PROBE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvit_probe.so")
+PROBE_SIGNATURES = {
+    "vit_probe_mfma": (_I, [_P, _I64, _I, _I, _P, _P]),
+    "vit_probe_last_error": (ctypes.c_char_p, []),
+}
+_probe = None
+
+
+def load_probe() -> ctypes.CDLL:
+    global _probe
+    with _lock:
+        if _probe is not None:
+            return _probe
+        if not os.path.exists(PROBE_PATH):
+            raise RuntimeError(f"{PROBE_PATH} is missing: build the HIP libraries first")
+        lib = ctypes.CDLL(PROBE_PATH)
+        for name, (res, args) in PROBE_SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _probe = lib
         return lib
 
 

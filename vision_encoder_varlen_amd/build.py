@@ -2,7 +2,9 @@
 
 Every HIP source under ``csrc/`` is compiled to an object in parallel, then
 linked into ``vision_encoder_varlen_amd/libvit.so`` next to this file, where the
-Python binding loads it.  Packed-fp32 VALU instructions are disabled for the
+Python binding loads it.  The MFMA-rate probe under ``probe/`` (measurement
+support, not part of the attention path) becomes a library of its own,
+``libvit_probe.so``.  Packed-fp32 VALU instructions are disabled for the
 device code.
 """
 from __future__ import annotations
@@ -20,6 +22,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libvit.so")
+PROBE_SRC = os.path.join(HERE, "probe", "probe.hip")
+PROBE_PATH = os.path.join(HERE, "libvit_probe.so")
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -118,9 +122,21 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
+    build_probe()
     if verbose:
-        print(f"built {LIB_PATH}", file=sys.stderr)
+        print(f"built {LIB_PATH} and {PROBE_PATH}", file=sys.stderr)
     return LIB_PATH
+
+
+def build_probe() -> str:
+    """Compile and link libvit_probe.so (the MFMA-rate probe); returns its path."""
+    tmp = PROBE_PATH + ".tmp"
+    cmd = [hipcc(), *COMMON_FLAGS, "-shared", "-o", tmp, PROBE_SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"probe build failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, PROBE_PATH)
+    return PROBE_PATH
 
 
 if __name__ == "__main__":

@@ -670,18 +670,6 @@ int vit_time_next_kernel(hipEvent_t start, hipEvent_t stop) {
   return ok();
 }
 
-int vit_probe_mfma(const void* operands, int64_t operand_bytes, int blocks, int iters, float* sink,
-                   hipStream_t stream) {
-  if (!operands || !sink) return fail(VIT_ERR_INVALID_ARG, "null pointer argument");
-  if (operand_bytes < vit::kProbeOperandBytes)
-    return fail(VIT_ERR_INVALID_ARG, "operands must hold %lld bytes", (long long)vit::kProbeOperandBytes);
-  if (!aligned16(operands) || !aligned4(sink)) return fail(VIT_ERR_INVALID_ARG, "misaligned buffer");
-  if (blocks < 1 || blocks > 65536 || iters < 1 || iters > (1 << 20))
-    return fail(VIT_ERR_INVALID_ARG, "blocks in [1, 65536] and iters in [1, 2^20] required");
-  const hipError_t e = vit::launch_probe_mfma(operands, blocks, iters, sink, stream);
-  return e == hipSuccess ? ok() : hip_fail(e, "probe launch");
-}
-
 const char* vit_last_error(void) { return g_last_error; }
 
 void vit_release(void) {

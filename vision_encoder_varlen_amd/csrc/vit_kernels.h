@@ -160,13 +160,5 @@ hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const Sc
 
 // Attention launches: lse (fp32 [T, H], may be null) receives each row's
 // log-sum-exp of scores, natural log.
-// MFMA rate probe: workgroups of kProbeThreads threads, each lane reading 256
-// operand bytes from slice blockIdx % kProbeSlices (kProbeOperandBytes in
-// all); each wave issues 32 * iters MFMAs of 32x32x16.
-constexpr int kProbeThreads = 256;
-constexpr int kProbeSlices = 64;
-constexpr int64_t kProbeOperandBytes = int64_t(kProbeSlices) * kProbeThreads * 256;
-hipError_t launch_probe_mfma(const void* operands, int blocks, int iters, float* sink,
-                             hipStream_t stream);
 
 }  // namespace vit

@@ -639,9 +639,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       for (int t = 0; t < STAGES - 1; ++t)
         if (t < ntiles) issue_tile(t);
     };
-    start_pass();
-    // The Q-side pre-pass runs while the pass's first tiles are in flight.
+    // The Q-side pre-pass runs before the pass's first tiles are issued: its
+    // register spills at D = 80 and 96 go through scratch, and a scratch
+    // reload issued behind the tile copies would wait for them (loads
+    // complete in order).
     if (q_pending) transform_q();
+    start_pass();
 
     auto run_pass = [&](auto m0_tag, auto m_tag, bool started) {
       if (!started) start_pass();

@@ -541,6 +541,8 @@ def main():
                                    "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
                                    "achieved_tflops": round(achieved, 3),
                                    "frac_of_bf16_peak": round(achieved / peak, 4)})
+    if is_bf16:
+        result["peak_on_box"] = peak_on_box(torch, dev)
     if ceiling is not None:
         result["mfma_ceiling"] = ceiling
         if not hbm_bound:
@@ -654,6 +656,33 @@ def mfma_ceiling(lib, torch, dev, stream):
     out["probe"] = ("vit_probe_mfma (libvit_probe.so): 512 workgroups x 4 waves, 4 independent "
                     "32x32x16 bf16 chains per wave")
     return out
+
+
+def peak_on_box(torch, dev):
+    """Dense bf16 MFMA peak computed on this machine: CUs x peak shader clock x
+    4096 FLOP per CU per clock.  Reads the clock and CU count through the HIP
+    runtime the process already has loaded (hipDeviceGetAttribute with
+    hipDeviceAttributeClockRate = 5, kHz, and
+    hipDeviceAttributeMultiprocessorCount = 63, the values of ROCm's
+    hip_runtime_api.h); None if the CU count read that way disagrees with
+    torch's (a sign of other enum values)."""
+    import ctypes
+    paths = sorted({line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line})
+    if not paths:
+        return None
+    hip = ctypes.CDLL(paths[0])
+    get = hip.hipDeviceGetAttribute
+    get.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+    get.restype = ctypes.c_int
+    idx = dev.index if dev.index is not None else 0
+    clk, cus = ctypes.c_int(0), ctypes.c_int(0)
+    if get(ctypes.byref(clk), 5, idx) != 0 or get(ctypes.byref(cus), 63, idx) != 0:
+        return None
+    if cus.value != torch.cuda.get_device_properties(idx).multi_processor_count:
+        return None
+    return {"cus": cus.value, "max_clock_mhz": round(clk.value / 1e3, 1),
+            "bf16_dense_tflops": round(cus.value * clk.value * 1e3 * 4096 / 1e12, 1),
+            "formula": "CUs x peak shader clock x 4096 bf16 FLOP per CU per clock"}
 
 
 def _traffic_path(workload):

@@ -58,7 +58,8 @@ PEAK_HBM_GBPS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--steps", type=int, default=400,
+                   help="timed steps (the attention is sampled on every --hook-every-th: 50 samples)")
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=2, help="seeded workload 1..5 (default 2)")
     p.add_argument("--no-cpu-baseline", action="store_true")

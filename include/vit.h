@@ -386,6 +386,34 @@ int vit_varlen_attn_planned_qnorm_rope(
     void* out, float* lse, const int64_t* strides, hipStream_t stream);
 
 /*
+ * vit_varlen_attn_planned with the whole pre-pass done inside the attention
+ * kernel, on q and on k: each work item normalises and rotates its query
+ * rows as vit_varlen_attn_planned_qnorm_rope does, and every K tile it
+ * visits is normalised (k_weight) and rotated in LDS before its scores are
+ * formed, so neither q nor k is read and written by a separate pre-pass.
+ * This is _qkv_with_rope (vLLM page: the q and k norms, then rotary on both)
+ * fused into the attention's tile loads, as the FA4 route on the tokenspeed
+ * page (MultimodalEncoderAttention.forward) fuses the rotary into the QKV
+ * split.  q and k in memory are not modified.
+ *  pos                  int32 [T, 2] (row, col), 8-byte aligned, or null.
+ *  q_weight, k_weight   fp32 [D], 16-byte aligned; both null (no norm) or
+ *                       both given, else VIT_ERR_INVALID_ARG.
+ *  theta, eps, rope_mode   as for vit_qk_norm_rope_ex (checked when used).
+ * Each unit transforms every K tile it visits, so a segment's keys are
+ * transformed once per q-tile of that segment (block_m rows each): the call
+ * pays where segments are short (one or two q-tiles).  Angles are reduced to
+ * a fraction of a turn exactly; the bf16 kernel then takes the hardware sine
+ * and cosine, the fp32 kernel sincosf.  Results match the separate pre-pass
+ * within the attention tolerance, not bit for bit.  Other arguments, layout
+ * and errors as for vit_varlen_attn_planned.
+ */
+int vit_varlen_attn_planned_qk_norm_rope(
+    const void* q, const void* k, const void* v, const int32_t* cu_seqlens, const int32_t* items,
+    int64_t cap, const int32_t* meta, int num_heads, int head_dim, float scale, int dtype,
+    int flags, const int32_t* pos, float theta, const float* q_weight, const float* k_weight,
+    float eps, int rope_mode, void* out, float* lse, const int64_t* strides, hipStream_t stream);
+
+/*
  * Reads (and with reset != 0 clears) the work-list error bits (enum
  * vit_worklist_error) left in the library's scratch by the most recent call
  * that builds its own work-list (vit_varlen_attn, _f32, _lse, _strided, _ex)

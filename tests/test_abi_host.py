@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
                      "vit_time_next_kernel", "vit_qk_norm_rope_worklist",
                      "vit_varlen_attn_lse", "vit_varlen_attn_strided",
                      "vit_qk_norm_rope_strided", "vit_dense_batch_attn", "vit_qk_norm_rope_ex",
-                     "vit_varlen_attn_ex", "vit_varlen_attn_planned_qnorm_rope"):
+                     "vit_varlen_attn_ex", "vit_varlen_attn_planned_qnorm_rope",
+                     "vit_varlen_attn_planned_qk_norm_rope"):
         assert required in names
     assert sorted(_lib.SIGNATURES) == names
 
@@ -329,6 +330,33 @@ def test_qnorm_rope_attention_argument_errors(lib):
     assert f(*head[:10], 7, *head[11:], *ok_q, out, None, None, None) == _lib.VIT_ERR_INVALID_ARG
     # an empty plan is a no-op
     assert f(*head[:5], 0, *head[6:], *ok_q, out, None, None, None) == _lib.VIT_OK
+
+
+def test_qk_norm_rope_attention_argument_errors(lib):
+    """vit_varlen_attn_planned_qk_norm_rope: the q-side checks, plus the pairing
+    and alignment of k_weight, all before any launch."""
+    f = lib.vit_varlen_attn_planned_qk_norm_rope
+    head = (FAKE, FAKE + 0x100, FAKE + 0x200, FAKE, FAKE, 4, FAKE + 0x40, 2, 64, 0.1, 1, 0)
+    out = FAKE + 0x1000
+    ok = (FAKE, 1e4, FAKE, FAKE + 0x80, 1e-6, 0)  # pos, theta, q_weight, k_weight, eps, rope_mode
+    bad = [((FAKE, 1e4, FAKE, FAKE + 0x80, 1e-6, 2), "rope_mode"),
+           ((FAKE + 4, 1e4, FAKE, FAKE + 0x80, 1e-6, 0), "pos must be 8-byte aligned"),
+           ((FAKE, 1e4, FAKE + 4, FAKE + 0x80, 1e-6, 0), "q_weight must be 16-byte aligned"),
+           ((FAKE, 1e4, FAKE, FAKE + 0x84, 1e-6, 0), "k_weight must be 16-byte aligned"),
+           ((FAKE, 1e4, FAKE, None, 1e-6, 0), "both"),
+           ((FAKE, 1e4, None, FAKE + 0x80, 1e-6, 0), "both"),
+           ((FAKE, -1.0, FAKE, FAKE + 0x80, 1e-6, 0), "theta"),
+           ((FAKE, 1e4, FAKE, FAKE + 0x80, -1.0, 0), "eps")]
+    for a, needle in bad:
+        assert f(*head, *a, out, None, None, None) == _lib.VIT_ERR_INVALID_ARG
+        assert needle in _err(lib), needle
+    assert f(*head[:10], 7, *head[11:], *ok, out, None, None, None) == _lib.VIT_ERR_INVALID_ARG
+    assert f(*head[:11], 2, *ok, out, None, None, None) == _lib.VIT_ERR_INVALID_ARG
+    assert "flags" in _err(lib)
+    # an empty plan is a no-op, with or without the norm
+    assert f(*head[:5], 0, *head[6:], *ok, out, None, None, None) == _lib.VIT_OK
+    assert f(*head[:5], 0, *head[6:], None, 1e4, None, None, 1e-6, 1, out, None, None,
+             None) == _lib.VIT_OK
 
 
 def test_noalloc_limits_and_errors_before_any_launch(lib):

@@ -1,8 +1,9 @@
 """Checks on the gfx950 assembly of the library's kernels, compiled here on the
 CPU (hipcc cross-compiles; no GPU is needed).
 
-* The attention kernel's global -> LDS copies are written as inline asm that
-  sets M0 (the LDS destination) right before each buffer load.  M0 is a
+* The attention kernel's global -> LDS copies (16 or 4 bytes per lane) are
+  written as inline asm that sets M0 (the LDS destination) right before each
+  buffer load.  M0 is a
   reserved register: the compiler does not save it around inline asm, so the
   asm is only safe while nothing else in the kernel keeps a value in M0.
   Every M0 reference must therefore be one of the asm's own pairs.
@@ -54,7 +55,7 @@ def test_m0_is_only_the_lds_copies_own(assembly):
         if not re.search(r"\bm0\b", l):
             continue
         if l.startswith("s_mov_b32 m0,"):
-            assert lines[i + 1].startswith("buffer_load_dwordx4") and lines[i + 1].endswith(" lds"), \
+            assert re.match(r"buffer_load_dword(x4)? ", lines[i + 1]) and lines[i + 1].endswith(" lds"), \
                 f"M0 set without the LDS copy after it: {l!r} then {lines[i + 1]!r}"
             copies += 1
         else:

@@ -49,6 +49,8 @@ SIGNATURES = {
     "vit_varlen_attn_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
     "vit_varlen_attn_planned_qnorm_rope": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _I, _F, _I, _I,
                                                 _P, _F, _P, _F, _I, _P, _P, _P, _P]),
+    "vit_varlen_attn_planned_qk_norm_rope": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _I, _F, _I,
+                                                  _I, _P, _F, _P, _P, _F, _I, _P, _P, _P, _P]),
     "vit_varlen_attn_strided": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),
     "vit_dense_batch_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
     "vit_varlen_attn_lse": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P]),

@@ -85,7 +85,7 @@ static_assert((int64_t)kPadOffset + kMaxSegmentBytes < (int64_t(1) << 32), "offs
 constexpr int odd_units(int u) { return (u & 1) ? u : u + 1; }
 constexpr int units_4_mod_8(int u) { return u % 8 == 4 ? u : units_4_mod_8(u + 1); }
 
-template <int D_, int WAVES_, int QB_, int BN_, int STAGES_, int OCC_>
+template <int D_, int WAVES_, int QB_, int BN_, int STAGES_, int OCC_, bool KF_ = false>
 struct Cfg {
   static constexpr int D = D_;
   static constexpr int WAVES = WAVES_;
@@ -93,6 +93,11 @@ struct Cfg {
   static constexpr int BN = BN_;                        // keys per tile
   static constexpr int STAGES = STAGES_;                // LDS ring depth
   static constexpr int OCC = OCC_;                      // waves per SIMD the kernel is built for
+  // KF: each K tile is normalised and rotated in LDS before its fragments
+  // are read; the tile's key positions (8 bytes per key) ride along with its
+  // copies (dword copies, so a segment's last key never shares a load with
+  // bytes past its end) into a region of their own.
+  static constexpr bool KF = KF_;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int WG_PER_CU = 4 * OCC / WAVES;     // resident workgroups per CU (4 SIMDs)
   static constexpr int BM = 32 * QB * WAVES;            // query rows per workgroup
@@ -104,7 +109,8 @@ struct Cfg {
   static constexpr int VSTR = units_4_mod_8(DU);        // V row stride (units)
   static constexpr int NK = (BN * KSTR + 63) / 64;      // copy instructions for K
   static constexpr int NV = (BN * VSTR + 63) / 64;      // copy instructions for V
-  static constexpr int NT = NK + NV;                    // copy instructions per tile
+  static constexpr int NP = KF ? BN / 32 : 0;           // dword copies of the keys' positions
+  static constexpr int NT = NK + NV + NP;               // copy instructions per tile
   // Instruction i goes to wave i % WAVES: the first NT % WAVES waves issue
   // NI_HI copies per tile, the others NI_LO.
   static constexpr int NI_LO = NT / WAVES;
@@ -114,7 +120,8 @@ struct Cfg {
   // and the transpose reads of head-dim columns D..32*DB-1 read at most one
   // row further.
   static constexpr int VREG = NV * 64 + VSTR;
-  static constexpr int STAGE_UNITS = KREG + VREG;
+  static constexpr int PREG = KF ? BN / 2 : 0;          // positions region (units), after V's
+  static constexpr int STAGE_UNITS = KREG + VREG + PREG;
   static constexpr int LDS_BYTES = STAGES * STAGE_UNITS * 16;
   static_assert(D % 16 == 0, "head dim must be a multiple of 16");
   static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
@@ -123,6 +130,7 @@ struct Cfg {
   static_assert(NI_HI * (STAGES - 2) <= 63, "vmcnt range");
   static_assert((4 * OCC) % WAVES == 0 && WG_PER_CU >= 1, "whole workgroups per CU");
   static_assert(LDS_BYTES * WG_PER_CU <= 160 * 1024, "LDS budget");
+  using WithK = Cfg<D_, WAVES_, QB_, BN_, STAGES_, OCC_, true>;
 };
 
 // The value lane l ^ 32 holds (v_permlane32_swap: a VALU exchange of the two
@@ -135,6 +143,21 @@ __device__ __forceinline__ float other_half(float x) {
 __device__ __forceinline__ float bf16_bits_to_f32(u16 b) { return __uint_as_float(unsigned(b) << 16); }
 __device__ __forceinline__ u16 f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(u16, (__bf16)x);  // round to nearest even
+}
+
+// Sum over aligned groups of N lanes (N = 2, 4 or 8) with DPP moves: lane
+// pairs, then quads, then the two quads of each 8-lane half row (mirrored).
+// Every lane of a group ends with the same bits (each step adds two values
+// that the partner lane adds in the other order).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 2 || N == 4 || N == 8, "group size");
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+  if constexpr (N >= 4)
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+  if constexpr (N >= 8)
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+  return x;
 }
 
 __device__ __forceinline__ int swap_bits_2_3(int x) {
@@ -167,6 +190,15 @@ __device__ __forceinline__ void wait_copies(int later) {
 // for its own copies explicitly.
 __device__ __forceinline__ void copy_to_lds(unsigned lds_byte, unsigned voffset, i32x4_t rsrc) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_byte), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// The same with 4 bytes per lane (LDS bytes [lds_byte + 4L, lds_byte + 4L + 4)):
+// each dword is inside the buffer's range or past it as a whole.
+__device__ __forceinline__ void copy_dword_to_lds(unsigned lds_byte, unsigned voffset, i32x4_t rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
                : "s"(lds_byte), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
@@ -213,18 +245,21 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
 
   // Per-lane byte offsets of this wave's copy instructions relative to the
   // tile's first key.  Instruction i = wave + WAVES*j (K units first, then V
-  // units); lanes that fall on row padding get an offset past num_records and
-  // write zeros.  With kSumByMfma the head-dim padding units of the V rows
-  // are not copied at all (cp_skip): they hold a constant 1 in dim D, written
-  // once below, so row D of V^T is all ones without any per-tile work.
+  // units, then with KF one for the keys' positions); lanes that fall on row
+  // padding get an offset past num_records and write zeros.  With kSumByMfma
+  // the head-dim padding units of the V rows are not copied at all (cp_skip):
+  // they hold a constant 1 in dim D, written once below, so row D of V^T is
+  // all ones without any per-tile work.
   const bool wave_hi = wave < C::NT % C::WAVES || C::NT % C::WAVES == 0;
   unsigned cp_off[NI];
   bool cp_is_k[NI];
+  bool cp_is_p[NI];
   bool cp_skip[NI];
   unsigned cp_lds[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int i = wave + C::WAVES * j;
+    const bool is_p = C::KF && i >= C::NK + C::NV;
     const bool is_k = i < C::NK;
     const int u = is_k ? i * 64 + lane : (i - C::NK) * 64 + lane;
     const int str = is_k ? C::KSTR : C::VSTR;
@@ -235,8 +270,15 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     cp_off[j] = data ? (unsigned(key) * unsigned(is_k ? ts.k : ts.v) + unsigned(col) * 8u) * 2u
                      : kPadOffset;
     cp_is_k[j] = is_k;
-    cp_skip[j] = kSumByMfma && !is_k && row < BN && col >= C::DU;
+    cp_is_p[j] = is_p;
+    cp_skip[j] = kSumByMfma && !is_k && !is_p && row < BN && col >= C::DU;
     cp_lds[j] = unsigned((is_k ? i * 64 : C::KREG + (i - C::NK) * 64) * 16);
+    if (is_p) {
+      // dword L of copy pi: int32 L & 1 (row, col) of key 32 pi + L / 2
+      const int pi = i - C::NK - C::NV;
+      cp_off[j] = unsigned(pi * 256 + lane * 4);
+      cp_lds[j] = unsigned((C::KREG + C::VREG) * 16 + pi * 256);
+    }
   }
   if constexpr (kSumByMfma) {
     // V row padding of every ring stage: unit DU starts with bf16 1.0 (dim D),
@@ -260,12 +302,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
   // the norm weights and the rotary frequencies (turns per unit coordinate,
   // hi + lo).
   __shared__ float s_qw[D];
+  __shared__ float s_kw[C::KF ? D : 1];
   __shared__ float2 s_rev[kMaxQFreqs];
-  static_assert((C::LDS_BYTES + D * 4 + kMaxQFreqs * 8) * C::WG_PER_CU <= 160 * 1024,
+  static_assert((C::LDS_BYTES + (C::KF ? 2 : 1) * D * 4 + kMaxQFreqs * 8) * C::WG_PER_CU <=
+                    160 * 1024,
                 "LDS budget with the pre-pass tables");
   const bool q_pending = qpre.pos != nullptr || qpre.weight != nullptr;
-  if (q_pending) {
+  if (q_pending || C::KF) {
     for (int i = tid; i < D; i += C::THREADS) s_qw[i] = qpre.weight != nullptr ? qpre.weight[i] : 1.f;
+    if constexpr (C::KF)
+      for (int i = tid; i < D; i += C::THREADS)
+        s_kw[i] = qpre.k_weight != nullptr ? qpre.k_weight[i] : 1.f;
     if (tid == 0)
       static_for<D / 4>([&](auto f_c) __attribute__((always_inline)) {
         constexpr int f = decltype(f_c)::value;
@@ -349,6 +396,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
                                   unsigned(((len - 1) * ts.k + D) * 2));
     const i32x4_t vrs = make_rsrc(v + size_t(start) * ts.v + size_t(h) * D,
                                   unsigned(((len - 1) * ts.v + D) * 2));
+    // KF: the segment's positions (8 bytes per key); without rotary a
+    // resource of zero bytes, so that copy only writes zeros.
+    i32x4_t prs{};
+    if constexpr (C::KF)
+      prs = qpre.pos != nullptr ? make_rsrc(qpre.pos + 2 * size_t(start), unsigned(len) * 8u)
+                                : make_rsrc(k, 0u);
 
     // Q^T fragments (B operand of S^T = K Q^T): lane holds 8 dims of its row
     // in each of the wave's QB query blocks: dims 16*st + 8*half + 0..7.
@@ -485,10 +538,108 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       const unsigned stage_lds = smem_base + unsigned((t % STAGES) * C::STAGE_UNITS * 16);
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        if ((j < C::NI_LO || wave_hi) && !cp_skip[j])
-          copy_to_lds(stage_lds + cp_lds[j], cp_off[j] + (cp_is_k[j] ? tile_off_k : tile_off_v),
-                      cp_is_k[j] ? krs : vrs);
+        if ((j < C::NI_LO || wave_hi) && !cp_skip[j]) {
+          if constexpr (C::KF) {
+            if (cp_is_p[j])
+              copy_dword_to_lds(stage_lds + cp_lds[j], cp_off[j] + unsigned(t) * unsigned(BN * 8), prs);
+            else
+              copy_to_lds(stage_lds + cp_lds[j], cp_off[j] + (cp_is_k[j] ? tile_off_k : tile_off_v),
+                          cp_is_k[j] ? krs : vrs);
+          } else {
+            copy_to_lds(stage_lds + cp_lds[j], cp_off[j] + (cp_is_k[j] ? tile_off_k : tile_off_v),
+                        cp_is_k[j] ? krs : vrs);
+          }
+        }
     };
+    // KF: RMSNorm then rotary on tile t's K rows in LDS, once per workgroup,
+    // in place, with the arithmetic of transform_q (fp32, one rounding to
+    // bf16).  CHP lanes share a key: lane c of them takes rotary pairs
+    // 8c .. 8c + 7, which lie in two 16-byte units of the row (dims 8c.. and
+    // D/2 + 8c.. for rotate-half, dims 16c .. 16c + 15 for complex), so every
+    // unit is read and written once.  The key's sum of squares is joined
+    // across its lanes with DPP.  Keys past the segment's end stay zero.  The
+    // positions arrive with the tile's copies (8 bytes per key, key order).
+    auto transform_k = [&](int t) __attribute__((always_inline)) {
+      constexpr int CH = D / 16;
+      constexpr int CHP = CH <= 2 ? 2 : (CH <= 4 ? 4 : 8);
+      static_assert(CH <= 8 && (D / 2) % 8 == 0, "rotary pairs must fill whole 16-byte units");
+      constexpr int ROUNDS = (BN * CHP + C::THREADS - 1) / C::THREADS;
+      u16* const kst = smem + (t % STAGES) * C::STAGE_UNITS * 8;
+      const int2* const kpos = reinterpret_cast<const int2*>(kst + (C::KREG + C::VREG) * 8);
+      const bool neox = qpre.rope_mode == 0;
+#pragma unroll
+      for (int rd = 0; rd < ROUNDS; ++rd) {
+        const int w = tid + rd * C::THREADS;
+        const int c = w % CHP;
+        const int row = w / CHP < BN ? w / CHP : BN - 1;  // LDS row; it holds key swap(row)
+        const int key = swap_bits_2_3(row);
+        const bool act = w / CHP < BN && c < CH && t * BN + key < len;
+        const int cc = c < CH ? c : CH - 1;  // idle lanes still compute, on valid indices
+        const int u0 = neox ? cc : 2 * cc;
+        const int u1 = neox ? cc + CH : 2 * cc + 1;
+        u32x4_t* const p0 = reinterpret_cast<u32x4_t*>(kst + (row * C::KSTR + u0) * 8);
+        u32x4_t* const p1 = reinterpret_cast<u32x4_t*>(kst + (row * C::KSTR + u1) * 8);
+        u32x4_t a = u32x4_t{0u, 0u, 0u, 0u}, b = a;
+        if (act) {
+          a = *p0;
+          b = *p1;
+        }
+        float x[16];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = __uint_as_float(a[e] << 16);
+          x[2 * e + 1] = __uint_as_float(a[e] & 0xffff0000u);
+          x[8 + 2 * e] = __uint_as_float(b[e] << 16);
+          x[8 + 2 * e + 1] = __uint_as_float(b[e] & 0xffff0000u);
+        }
+        if (qpre.k_weight != nullptr) {
+          float ss = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) ss = fmaf(x[i], x[i], ss);
+          ss = group_sum<CHP>(ss);
+          const float rinv = rsqrtf(ss * (1.f / D) + qpre.eps);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            x[i] = x[i] * rinv * s_kw[neox ? 8 * cc + i : 16 * cc + i];
+            x[8 + i] = x[8 + i] * rinv * s_kw[neox ? D / 2 + 8 * cc + i : 16 * cc + 8 + i];
+          }
+        }
+        if (qpre.pos != nullptr) {
+          const int2 pc = act ? kpos[key] : make_int2(0, 0);
+#pragma unroll
+          for (int pr = 0; pr < 8; ++pr) {
+            const int m = 8 * cc + pr;  // pair index
+            const bool on_row = m < D / 4;
+            const float coord = float(on_row ? pc.x : pc.y);
+            const float2 rv = s_rev[on_row ? m : m - D / 4];
+            const float tt = coord * rv.x;
+            const float frac = (tt - rintf(tt)) + (fmaf(coord, rv.x, -tt) + coord * rv.y);
+            const float cs = __builtin_amdgcn_cosf(frac);
+            const float sn = __builtin_amdgcn_sinf(frac);
+            if (neox) {
+              const float lo = x[pr], hi = x[8 + pr];
+              x[pr] = lo * cs - hi * sn;
+              x[8 + pr] = hi * cs + lo * sn;
+            } else {
+              const float e0 = x[2 * pr], e1 = x[2 * pr + 1];
+              x[2 * pr] = e0 * cs - e1 * sn;
+              x[2 * pr + 1] = e1 * cs + e0 * sn;
+            }
+          }
+        }
+        if (act) {
+          bf16x8_t y0, y1;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            y0[i] = (__bf16)x[i];
+            y1[i] = (__bf16)x[8 + i];
+          }
+          *p0 = __builtin_bit_cast(u32x4_t, y0);
+          *p1 = __builtin_bit_cast(u32x4_t, y1);
+        }
+      }
+    };
+
     // Sum of p over the whole row b (both lane halves).
     auto row_total = [&](int b) {
       if constexpr (kSumByMfma) {
@@ -517,6 +668,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       else wait_copies<C::NI_LO, STAGES>(later);
       __syncthreads();  // everyone's copies of tile t landed; tile t-1 is free
       if (t + STAGES - 1 < ntiles) issue_tile(t + STAGES - 1);
+      if constexpr (C::KF) {
+        transform_k(t);  // every wave takes part, active or not
+        __syncthreads();  // tile t's K rows are normalised and rotated
+      }
       if (!wave_active) return;
       const int kv0 = t * BN;
       // Causal: a tile that starts after this wave's last row adds nothing.
@@ -665,13 +820,22 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       // Tiles before nfull need no mask: every key is inside the segment and
       // (causal) at or before the unit's first query row.  The rest are masked.
       const int nfull = CAUSAL ? min(len, qt * C::BM + 1) / BN : len / BN;
+      // With KF the tile body outgrows the inliner's budget; its calls are
+      // inlined by force (the other kernels' code is left as it was).
+      auto tile = [&](auto masked_tag, auto mode_tag, int t) __attribute__((always_inline)) {
+        if constexpr (C::KF) {
+          [[clang::always_inline]] process_tile(masked_tag, mode_tag, t);
+        } else {
+          process_tile(masked_tag, mode_tag, t);
+        }
+      };
       if (nfull == 0) {
-        process_tile(std::true_type{}, m0_tag, 0);
+        tile(std::true_type{}, m0_tag, 0);
       } else {
-        process_tile(std::false_type{}, m0_tag, 0);
-        for (int t = 1; t < nfull; ++t) process_tile(std::false_type{}, m_tag, t);
+        tile(std::false_type{}, m0_tag, 0);
+        for (int t = 1; t < nfull; ++t) tile(std::false_type{}, m_tag, t);
       }
-      for (int t = nfull > 1 ? nfull : 1; t < ntiles; ++t) process_tile(std::true_type{}, m_tag, t);
+      for (int t = nfull > 1 ? nfull : 1; t < ntiles; ++t) tile(std::true_type{}, m_tag, t);
     };
 
     run_pass(std::integral_constant<int, kSetRef>{}, std::integral_constant<int, kPlain>{}, true);
@@ -720,6 +884,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
 }
 
 template <class C>
+auto pick_kernel(bool causal, bool pos_scale) {
+  return causal ? (pos_scale ? attn_bf16_kernel<C, true, true> : attn_bf16_kernel<C, false, true>)
+                : (pos_scale ? attn_bf16_kernel<C, true, false> : attn_bf16_kernel<C, false, false>);
+}
+
+template <class C>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, const Schedule& sch, int H,
                       float scale, bool causal, const QPrepass* qp, void* out, float* lse,
                       TokenStrides ts, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
@@ -735,8 +905,9 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, const Schedul
   // A multiple of 8 workgroups, so each keeps its XCD across its units.
   const int64_t grid = ((units < kMaxAttnGridBf16 ? units : kMaxAttnGridBf16) + 7) / 8 * 8;
   const float c = scale * kLog2e;
-  auto kern = causal ? (c > 0.f ? attn_bf16_kernel<C, true, true> : attn_bf16_kernel<C, false, true>)
-                    : (c > 0.f ? attn_bf16_kernel<C, true, false> : attn_bf16_kernel<C, false, false>);
+  static_assert(C::WithK::THREADS == C::THREADS && C::WithK::BM == C::BM, "same launch shape");
+  auto kern = qpre.fuse_k ? pick_kernel<typename C::WithK>(causal, c > 0.f)
+                          : pick_kernel<C>(causal, c > 0.f);
   hipExtLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(C::THREADS), 0, stream, e0, e1, 0,
                      static_cast<const u16*>(q), static_cast<const u16*>(k),
                      static_cast<const u16*>(v), sch.items, sch.meta, (long long)sch.cap, sch.batch,

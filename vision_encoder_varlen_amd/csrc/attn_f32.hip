@@ -75,54 +75,62 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
 #pragma unroll
       for (int d = 0; d < HD; ++d) qv[d] = 0.f;
     }
-    // Q-side pre-pass (RMSNorm then rotary, fp32).  This lane holds dims
-    // half * D/2 + d: rotate-half partners sit in the other half of the wave
-    // at the same d; complex partners are d ^ 1 in this lane.
-    if (qpre.weight != nullptr) {
-      float ss = 0.f;
+    // Pre-pass on one row held by a lane pair (RMSNorm with `weight`, then
+    // rotary at `pr`; fp32).  This lane holds dims half * D/2 + d: rotate-half
+    // partners sit in the other half of the wave at the same d; complex
+    // partners are d ^ 1 in this lane.  Used for the query row, and with
+    // fuse_k for each key row of a tile.
+    auto prep_row = [&](float (&xv)[HD], const float* weight, int2 pr) {
+      if (weight != nullptr) {
+        float ss = 0.f;
 #pragma unroll
-      for (int d = 0; d < HD; ++d) ss = fmaf(qv[d], qv[d], ss);
-      ss += __shfl_xor(ss, 32);
-      const float rinv = rsqrtf(ss * (1.f / D) + qpre.eps);
+        for (int d = 0; d < HD; ++d) ss = fmaf(xv[d], xv[d], ss);
+        ss += __shfl_xor(ss, 32);
+        const float rinv = rsqrtf(ss * (1.f / D) + qpre.eps);
 #pragma unroll
-      for (int d = 0; d < HD; ++d) qv[d] = qv[d] * rinv * qpre.weight[half * HD + d];
-    }
-    if (qpre.pos != nullptr) {
-      int2 pr = make_int2(0, 0);
-      if (qrow < len) pr = *reinterpret_cast<const int2*>(qpre.pos + 2 * (start + qrow));
-      // Angle of frequency F on the row (col = false) or column axis:
-      // 2*pi * coord * rev[F], reduced to a fraction of a turn exactly, then an
-      // accurate sincosf.  F is a compile-time constant (no dynamic indexing
-      // of the parameter block).
-      auto cos_sin = [&](auto f_c, bool col) {
-        constexpr int F = decltype(f_c)::value;
-        const float c = float(col ? pr.y : pr.x);
-        const float t = c * qpre.rev_hi[F];
-        const float frac = (t - rintf(t)) + (fmaf(c, qpre.rev_hi[F], -t) + c * qpre.rev_lo[F]);
-        float sn, cn;
-        sincosf(6.283185307179586f * frac, &sn, &cn);
-        return make_float2(cn, sn);
-      };
-      if (qpre.rope_mode == 0) {
-        // pair index j = d for both halves
-        static_for<HD>([&](auto d_c) {
-          constexpr int d = decltype(d_c)::value;
-          const float part = __shfl_xor(qv[d], 32);
-          const float2 cs = cos_sin(std::integral_constant<int, (d < D / 4 ? d : d - D / 4)>{},
-                                    d >= D / 4);
-          qv[d] = half == 0 ? qv[d] * cs.x - part * cs.y : qv[d] * cs.x + part * cs.y;
-        });
-      } else {
-        // pair index j = half * D/4 + d/2: the row axis in half 0, the column
-        // axis in half 1, frequency d/2 in both
-        static_for<HD / 2>([&](auto i_c) {
-          constexpr int d = 2 * decltype(i_c)::value;
-          const float2 cs = cos_sin(std::integral_constant<int, d / 2>{}, half != 0);
-          const float a = qv[d], b = qv[d + 1];
-          qv[d] = a * cs.x - b * cs.y;
-          qv[d + 1] = b * cs.x + a * cs.y;
-        });
+        for (int d = 0; d < HD; ++d) xv[d] = xv[d] * rinv * weight[half * HD + d];
       }
+      if (qpre.pos != nullptr) {
+        // Angle of frequency F on the row (col = false) or column axis:
+        // 2*pi * coord * rev[F], reduced to a fraction of a turn exactly, then
+        // an accurate sincosf.  F is a compile-time constant (no dynamic
+        // indexing of the parameter block).
+        auto cos_sin = [&](auto f_c, bool col) {
+          constexpr int F = decltype(f_c)::value;
+          const float c = float(col ? pr.y : pr.x);
+          const float t = c * qpre.rev_hi[F];
+          const float frac = (t - rintf(t)) + (fmaf(c, qpre.rev_hi[F], -t) + c * qpre.rev_lo[F]);
+          float sn, cn;
+          sincosf(6.283185307179586f * frac, &sn, &cn);
+          return make_float2(cn, sn);
+        };
+        if (qpre.rope_mode == 0) {
+          // pair index j = d for both halves
+          static_for<HD>([&](auto d_c) {
+            constexpr int d = decltype(d_c)::value;
+            const float part = __shfl_xor(xv[d], 32);
+            const float2 cs = cos_sin(std::integral_constant<int, (d < D / 4 ? d : d - D / 4)>{},
+                                      d >= D / 4);
+            xv[d] = half == 0 ? xv[d] * cs.x - part * cs.y : xv[d] * cs.x + part * cs.y;
+          });
+        } else {
+          // pair index j = half * D/4 + d/2: the row axis in half 0, the
+          // column axis in half 1, frequency d/2 in both
+          static_for<HD / 2>([&](auto i_c) {
+            constexpr int d = 2 * decltype(i_c)::value;
+            const float2 cs = cos_sin(std::integral_constant<int, d / 2>{}, half != 0);
+            const float a = xv[d], b = xv[d + 1];
+            xv[d] = a * cs.x - b * cs.y;
+            xv[d + 1] = b * cs.x + a * cs.y;
+          });
+        }
+      }
+    };
+    if (qpre.weight != nullptr || qpre.pos != nullptr) {
+      int2 pr = make_int2(0, 0);
+      if (qpre.pos != nullptr && qrow < len)
+        pr = *reinterpret_cast<const int2*>(qpre.pos + 2 * (start + qrow));
+      prep_row(qv, qpre.weight, pr);
     }
     float m = -INFINITY, l = 0.f;
     // Keys visited: the segment, or with CAUSAL those up to the unit's last row.
@@ -144,6 +152,20 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
       }
       __syncthreads();
       const int nk = kv_end - kv0 < kBN ? kv_end - kv0 : kBN;
+      if (qpre.fuse_k && r < nk) {
+        // fuse_k: key row r of the tile, normalised and rotated in place by
+        // its lane pair (both lanes of a pair take this branch together)
+        float* const kr = ks + r * ROW + half * HD;
+        float kv[HD];
+#pragma unroll
+        for (int d = 0; d < HD; ++d) kv[d] = kr[d];
+        int2 pr = make_int2(0, 0);
+        if (qpre.pos != nullptr) pr = *reinterpret_cast<const int2*>(qpre.pos + 2 * (start + kv0 + r));
+        prep_row(kv, qpre.k_weight, pr);
+#pragma unroll
+        for (int d = 0; d < HD; ++d) kr[d] = kv[d];
+      }
+      if (qpre.fuse_k) __syncthreads();
       for (int j = 0; j < nk; ++j) {
         const float* kr = ks + j * ROW + half * HD;
         float part = 0.f;

@@ -613,6 +613,42 @@ int vit_varlen_attn_planned_qnorm_rope(
                      head_dim, scale, dtype, flags, out, lse, ts, stream, t, &qp);
 }
 
+int vit_varlen_attn_planned_qk_norm_rope(
+    const void* q, const void* k, const void* v, const int32_t* cu_seqlens, const int32_t* items,
+    int64_t cap, const int32_t* meta, int num_heads, int head_dim, float scale, int dtype,
+    int flags, const int32_t* pos, float theta, const float* q_weight, const float* k_weight,
+    float eps, int rope_mode, void* out, float* lse, const int64_t* strides, hipStream_t stream) {
+  const TimingHook t = take_timing();
+  if (!items || !meta) return fail(VIT_ERR_INVALID_ARG, "null work-list pointer");
+  if (!aligned16(items)) return fail(VIT_ERR_INVALID_ARG, "items must be 16-byte aligned");
+  if (dtype != VIT_F32 && dtype != VIT_BF16) return fail(VIT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  int rc = check_attn_args(q, k, v, cu_seqlens, 0, 0, num_heads, head_dim, scale, out);
+  if (rc != VIT_OK) return rc;
+  rc = check_flags(flags);
+  if (rc != VIT_OK) return rc;
+  if (cap < 0 || cap > kMaxCapacity) return fail(VIT_ERR_INVALID_ARG, "bad work-list capacity %lld", (long long)cap);
+  rc = check_lse(lse, q, k, v, out);
+  if (rc != VIT_OK) return rc;
+  vit::TokenStrides ts{};
+  rc = make_strides(strides, 4, num_heads, head_dim, dtype, &ts);
+  if (rc != VIT_OK) return rc;
+  if ((q_weight == nullptr) != (k_weight == nullptr))
+    return fail(VIT_ERR_INVALID_ARG, "q_weight and k_weight must both be given or both be null");
+  if (k_weight != nullptr && !aligned16(k_weight))
+    return fail(VIT_ERR_INVALID_ARG, "k_weight must be 16-byte aligned");
+  vit::QPrepass qp{};
+  rc = make_qprepass(head_dim, pos, theta, q_weight, eps, rope_mode, &qp);
+  if (rc != VIT_OK) return rc;
+  qp.k_weight = k_weight;
+  qp.fuse_k = 1;
+  if (cap == 0) {
+    const hipError_t e = record_empty(t, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "hipEventRecord");
+  }
+  return launch_attn(q, k, v, vit::Schedule{cu_seqlens, items, meta, cap, 0, 0}, num_heads,
+                     head_dim, scale, dtype, flags, out, lse, ts, stream, t, &qp);
+}
+
 int vit_dense_batch_attn(const void* q, const void* k, const void* v, int batch, int seq_len,
                          int num_heads, int head_dim, float scale, int dtype, int flags,
                          void* out, float* lse, const int64_t* strides, hipStream_t stream) {

@@ -30,19 +30,23 @@ __host__ __device__ __attribute__((always_inline)) inline void static_for(F&& f)
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Q-side pre-pass applied by the attention kernels to each query row as they
-// load it (pos == null and weight == null: none).  The rotation angle of pair
-// index j for coordinate c is 2*pi * c * rev[j] with rev[j] = inv_freq[j] /
-// (2*pi) held as an unevaluated sum rev_hi[j] + rev_lo[j], so the angle can be
-// reduced to a fraction of a turn exactly before the hardware sine and cosine.
+// Pre-pass applied by the attention kernels themselves: to each query row as
+// they load it (pos == null and weight == null: none), and with fuse_k also to
+// each key row of every K tile (k_weight, same pos and rotary).  The rotation
+// angle of pair index j for coordinate c is 2*pi * c * rev[j] with rev[j] =
+// inv_freq[j] / (2*pi) held as an unevaluated sum rev_hi[j] + rev_lo[j], so
+// the angle can be reduced to a fraction of a turn exactly before the hardware
+// sine and cosine.
 constexpr int kMaxQFreqs = 32;  // D/4 for D <= 128
 struct QPrepass {
   const int32_t* pos;    // int32 [T, 2] (row, col), or null: no rotary
-  const float* weight;   // fp32 [D] RMSNorm weight, or null: no norm
+  const float* weight;   // fp32 [D] RMSNorm weight of q, or null: no norm
   float eps;
   int rope_mode;         // 0: rotate-half pairs (m, m + D/2); 1: pairs (2j, 2j + 1)
   float rev_hi[kMaxQFreqs];
   float rev_lo[kMaxQFreqs];
+  const float* k_weight; // fp32 [D] RMSNorm weight of k (fuse_k), or null: no norm
+  int fuse_k;            // 1: k's rows are normalised and rotated in the kernel too
 };
 
 // Where the attention kernels take their (segment, q-tile) items from: a

@@ -408,6 +408,54 @@ def varlen_attn_planned_qnorm_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Te
     return out
 
 
+def varlen_attn_planned_qk_norm_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                     cu_seqlens: torch.Tensor, plan: Plan,
+                                     pos: Optional[torch.Tensor], theta: float = 10000.0,
+                                     q_weight: Optional[torch.Tensor] = None,
+                                     k_weight: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                                     rope_mode: str = "neox", scale: Optional[float] = None,
+                                     out: Optional[torch.Tensor] = None,
+                                     lse: Optional[torch.Tensor] = None,
+                                     causal: bool = False) -> torch.Tensor:
+    """``varlen_attn_planned`` with the RMSNorm + rotary of both q and k applied
+    inside the kernel (q and k themselves are left unchanged): no separate
+    pre-pass.  ``q_weight`` and ``k_weight`` are both given or both None."""
+    _attn_checks(q, k, v, cu_seqlens)
+    T, H, D = q.shape
+    if plan.block_m != attn_block_m(H, D, q.dtype):
+        raise ValueError("plan was built with a different block_m than this kernel uses")
+    _check_plan_span(plan, k, v)
+    if pos is not None:
+        _need_cuda("pos", pos, torch.int32)
+        if pos.shape != (T, 2):
+            raise ValueError("pos must be int32 [T, 2]")
+    if (q_weight is None) != (k_weight is None):
+        raise ValueError("q_weight and k_weight must both be given or both be None")
+    for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
+        if w is not None:
+            _need_cuda(name, w, torch.float32)
+            if w.shape != (D,):
+                raise ValueError(f"{name} must be float32 [D]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_cuda("out", out, q.dtype, token_strided=True)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if lse is not None:
+        _need_cuda("lse", lse, torch.float32)
+        if lse.shape != (T, H):
+            raise ValueError("lse must be float32 [T, H]")
+    _lib.check(_lib.load().vit_varlen_attn_planned_qk_norm_rope(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), plan.items.data_ptr(),
+        plan.cap, plan.meta.data_ptr(), H, D, float(scale), dtype_code(q.dtype), _flags(causal),
+        _ptr(pos), float(theta), _ptr(q_weight), _ptr(k_weight), float(eps),
+        _rope_mode(rope_mode), out.data_ptr(), _ptr(lse), _strides(q, k, v, out), _stream(q)))
+    return out
+
+
 def device_error(reset: bool = False, device: Optional[torch.device] = None) -> int:
     """Work-list error bits of the last ``varlen_attn`` on the current stream (syncs it)."""
     import ctypes

@@ -71,6 +71,9 @@ def parse():
     p.add_argument("--fuse-q", action="store_true",
                    help="q's RMSNorm + rotary inside the attention kernel; the pre-pass "
                         "launch handles k only")
+    p.add_argument("--fuse-qk", action="store_true",
+                   help="the whole pre-pass (q and k) inside the attention kernel; the step's "
+                        "first launch only builds the work-list")
     p.add_argument("--dense-batch", action="store_true",
                    help="uniform workloads only: attention through vit_dense_batch_attn "
                         "(cu_seqlens = None form: no work-list, no metadata reads)")
@@ -363,6 +366,22 @@ def main():
                    float(wl.softmax_scale), dcode, flags, pos.data_ptr(), float(wl.theta), wq_p,
                    float(wl.eps), 0, out.data_ptr(), None, fq_strides, sh)
         at_lse_args = at_args[:-3] + (lse_buf.data_ptr(), fq_strides, sh)
+    if args.fuse_qk:
+        if args.dense_batch or args.fuse_q:
+            sys.exit("bench: --fuse-qk times the work-list step alone; drop --dense-batch / --fuse-q")
+        # no pre-pass launch: the step's first launch builds the work-list, and
+        # the attention kernel normalises and rotates q and k from q_src, k_src
+        f_pre = f_fused = f_wl
+        pre_args = fused_args = wl_args
+        f_at = lib.vit_varlen_attn_planned_qk_norm_rope
+        fqk_strides = None
+        if args.packed_qkv:
+            fqk_strides = (ctypes.c_int64 * 4)(q_src.stride(0), k_src.stride(0), v.stride(0), H * D)
+        at_args = (q_src.data_ptr(), k_src.data_ptr(), v.data_ptr(), cu.data_ptr(),
+                   plan.items.data_ptr(), plan.cap, plan.meta.data_ptr(), H, D,
+                   float(wl.softmax_scale), dcode, flags, pos.data_ptr(), float(wl.theta), wq_p,
+                   wk_p, float(wl.eps), 0, out.data_ptr(), None, fqk_strides, sh)
+        at_lse_args = at_args[:-3] + (lse_buf.data_ptr(), fqk_strides, sh)
 
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -507,7 +526,8 @@ def main():
         "config": {"workload": wl.name + ("_packed_qkv" if args.packed_qkv else "")
                    + ("_dense_batch" if args.dense_batch else "")
                    + ("_causal" if args.causal else "")
-                   + ("_fused_q" if args.fuse_q else ""),
+                   + ("_fused_q" if args.fuse_q else "")
+                   + ("_fused_qk" if args.fuse_qk else ""),
                    "images": wl.num_seqs, "tokens": T, "heads": H,
                    "head_dim": D, "max_seqlen": wl.max_seqlen, "qk_norm": wl.use_norm,
                    "rope": "2d", "flops_per_step": flops, "parallelism": "none (1 GPU)"},
@@ -548,8 +568,15 @@ def main():
         result["mfma_ceiling"] = ceiling
         if not hbm_bound:
             result["roofline"]["frac_of_random_operand_ceiling"] = round(achieved / ceiling["random_bf16"], 4)
+    if args.fuse_qk:
+        # no pre-pass kernel to report: the side loops above timed the work-list build
+        result["prepass"] = {"note": "none: q and k are normalised and rotated inside the "
+                                     "attention kernel (vit_varlen_attn_planned_qk_norm_rope)"}
+        result["kernels_us"] = {k: v for k, v in result["kernels_us"].items()
+                                if k not in ("prepass_alone", "prepass_cache_warm",
+                                             "prepass_and_worklist_launch")}
     if args.second_target and args.config == 2 and not (args.causal or args.fuse_q or args.dense_batch
-                                                         or args.packed_qkv):
+                                                         or args.packed_qkv or args.fuse_qk):
         result["second_target"] = second_target(args.second_target, lib, torch, dev, stream,
                                                 max(K, 50), new_events, args.settle_ms)
     if not args.no_cpu_baseline:
@@ -694,7 +721,7 @@ def _kernel_sha():
     """Hash of the attention kernel's sources (the kernel and its launch header)."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("attn_bf16.hip", "vit_kernels.h"):
+    for name in ("attn_bf16.hip", "attn_bf16_kernel.h", "vit_kernels.h"):
         with open(os.path.join(ROOT, "vision_encoder_varlen_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -48,21 +48,26 @@ def _code(lines):
     return [l.split(";")[0].strip() for l in lines if l.strip() and not l.strip().startswith(";")]
 
 
+ATTN_UNITS = ("attn_bf16.hip", "attn_bf16_fused.hip")
+
+
 def test_m0_is_only_the_lds_copies_own(assembly):
-    lines = _code(assembly["attn_bf16.hip"])
-    copies = 0
-    for i, l in enumerate(lines):
-        if not re.search(r"\bm0\b", l):
-            continue
-        if l.startswith("s_mov_b32 m0,"):
-            assert re.match(r"buffer_load_dword(x4)? ", lines[i + 1]) and lines[i + 1].endswith(" lds"), \
-                f"M0 set without the LDS copy after it: {l!r} then {lines[i + 1]!r}"
-            copies += 1
-        else:
-            pytest.fail(f"M0 used outside the LDS copy asm: {l!r}")
-    assert copies > 0
+    for unit in ATTN_UNITS:
+        lines = _code(assembly[unit])
+        copies = 0
+        for i, l in enumerate(lines):
+            if not re.search(r"\bm0\b", l):
+                continue
+            if l.startswith("s_mov_b32 m0,"):
+                assert re.match(r"buffer_load_dword(x4)? ", lines[i + 1]) and \
+                    lines[i + 1].endswith(" lds"), \
+                    f"{unit}: M0 set without the LDS copy after it: {l!r} then {lines[i + 1]!r}"
+                copies += 1
+            else:
+                pytest.fail(f"{unit}: M0 used outside the LDS copy asm: {l!r}")
+        assert copies > 0, unit
     for name, src in assembly.items():
-        if name != "attn_bf16.hip":
+        if name not in ATTN_UNITS:
             assert not any(re.search(r"\bm0\b", l) for l in _code(src)), name
 
 

@@ -156,6 +156,12 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const S
                             int H, int D, float scale, bool causal, const QPrepass* qp, void* out,
                             float* lse, TokenStrides ts, hipStream_t stream, hipEvent_t ev_start,
                             hipEvent_t ev_stop);
+// The same for calls with part of the pre-pass inside the kernel (qp not
+// null, with pos, a q weight or fuse_k): the kernels of attn_bf16_fused.hip.
+hipError_t launch_attn_bf16_fused(const void* q, const void* k, const void* v, const Schedule& sch,
+                                  int H, int D, float scale, bool causal, const QPrepass* qp,
+                                  void* out, float* lse, TokenStrides ts, hipStream_t stream,
+                                  hipEvent_t ev_start, hipEvent_t ev_stop);
 
 hipError_t launch_attn_f32(const void* q, const void* k, const void* v, const Schedule& sch,
                            int H, int D, float scale, bool causal, const QPrepass* qp, void* out,

@@ -613,11 +613,61 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[st][i] = y[st][i];
           };
+          // Table reads by runs: the 8 elements of register st hold 8
+          // consecutive rotary pairs of one coordinate (rotate-half, D a
+          // multiple of 32) or 4 (complex), so their cos and sin are one run
+          // of the table (16-byte reads instead of one read and an address
+          // per element).
+          auto rope_rows_runs = [&]() __attribute__((always_inline)) {
+            float y[KS][8];
+            if (qpre.rope_mode == 0) {
+              if constexpr (D % 32 == 0) {
+#pragma unroll
+                for (int st = 0; st < KS; ++st) {
+                  // D/2 is a multiple of 16, so whether dims 16st + 8half ..
+                  // + 7 are in the first half does not depend on half
+                  constexpr int kFirstRegs = HALF / 16;
+                  const bool first = st < kFirstRegs;
+                  const int m0 = 16 * st + 8 * half - (first ? 0 : HALF);
+                  const bool on_row = m0 < QUART;
+                  const float2* tb = s_cs + (on_row ? pc.x : pc.y) * QUART + (on_row ? m0 : m0 - QUART);
+#pragma unroll
+                  for (int i = 0; i < 8; ++i) {
+                    const float partner = x[(st + HALF / 16) % KS][i];
+                    const float2 v = tb[i];
+                    y[st][i] = first ? x[st][i] * v.x - partner * v.y : x[st][i] * v.x + partner * v.y;
+                  }
+                }
+              }
+            } else {
+#pragma unroll
+              for (int st = 0; st < KS; ++st) {
+                const int j0 = 8 * st + 4 * half;
+                const bool on_row = j0 < QUART;
+                const float2* tb = s_cs + (on_row ? pc.x : pc.y) * QUART + (on_row ? j0 : j0 - QUART);
+#pragma unroll
+                for (int i = 0; i < 8; i += 2) {
+                  const float2 v = tb[i / 2];
+                  y[st][i] = x[st][i] * v.x - x[st][i + 1] * v.y;
+                  y[st][i + 1] = x[st][i + 1] * v.x + x[st][i] * v.y;
+                }
+              }
+            }
+#pragma unroll
+            for (int st = 0; st < KS; ++st)
+#pragma unroll
+              for (int i = 0; i < 8; ++i) x[st][i] = y[st][i];
+          };
+          static_assert(QUART % 4 == 0, "complex pairs of a register share a coordinate");
           if constexpr (C::QT) {
-            if (__all(unsigned(pc.x) < unsigned(kRopeCoords) && unsigned(pc.y) < unsigned(kRopeCoords)))
-              rope_rows(cossin_table);
-            else
+            if (__all(unsigned(pc.x) < unsigned(kRopeCoords) && unsigned(pc.y) < unsigned(kRopeCoords))) {
+              if (D % 32 == 0 || qpre.rope_mode != 0)
+                rope_rows_runs();
+              else
+                rope_rows(cossin_table);  // rotate-half at D = 80: runs cross the row/column split
+            } else {
               rope_rows(cossin_direct);
+            }
           } else {
             rope_rows(cossin_direct);
           }
@@ -681,7 +731,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       constexpr int ROUNDS = (BN * CHP + C::THREADS - 1) / C::THREADS;
       u16* const kst = smem + (t % STAGES) * C::STAGE_UNITS * 8;
       const int2* const kpos = reinterpret_cast<const int2*>(kst + (C::KREG + C::VREG) * 8);
-      const bool neox = qpre.rope_mode == 0;
+      // One code path per rotary pairing (a uniform branch, taken once per
+      // tile), so no element is computed both ways and selected.
+      auto run = [&](auto neox_tag) __attribute__((always_inline)) {
+      constexpr bool neox = decltype(neox_tag)::value;
 #pragma unroll
       for (int rd = 0; rd < ROUNDS; ++rd) {
         const int w = tid + rd * C::THREADS;
@@ -713,10 +766,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
           for (int i = 0; i < 16; ++i) ss = fmaf(x[i], x[i], ss);
           ss = group_sum<CHP>(ss);
           const float rinv = rsqrtf(ss * (1.f / D) + qpre.eps);
+          const float* w0 = s_kw + (neox ? 8 * cc : 16 * cc);  // weights of x[0..7]
+          const float* w1 = s_kw + (neox ? D / 2 + 8 * cc : 16 * cc + 8);  // of x[8..15]
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            x[i] = x[i] * rinv * s_kw[neox ? 8 * cc + i : 16 * cc + i];
-            x[8 + i] = x[8 + i] * rinv * s_kw[neox ? D / 2 + 8 * cc + i : 16 * cc + 8 + i];
+            x[i] = x[i] * rinv * w0[i];
+            x[8 + i] = x[8 + i] * rinv * w1[i];
           }
         }
         if (qpre.pos != nullptr) {
@@ -728,8 +783,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
               const int m = 8 * cc + pr;
               const bool on_row = m < D / 4;
               float cs, sn;
-              cossin(on_row ? pc.x : pc.y, on_row ? m : m - D / 4, cs, sn);
-              if (neox) {
+              cossin(pr, on_row ? pc.x : pc.y, on_row ? m : m - D / 4, cs, sn);
+              if constexpr (neox) {
                 const float lo = x[pr], hi = x[8 + pr];
                 x[pr] = lo * cs - hi * sn;
                 x[8 + pr] = hi * cs + lo * sn;
@@ -741,13 +796,24 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
             }
           };
           if (__all(unsigned(pc.x) < unsigned(kRopeCoords) && unsigned(pc.y) < unsigned(kRopeCoords))) {
-            rotate([&](int ci, int f, float& cs, float& sn) {
-              const float2 v = s_cs[ci * (D / 4) + f];
-              cs = v.x;
-              sn = v.y;
-            });
+            if constexpr ((D / 4) % 8 == 0) {
+              // pairs 8 cc .. 8 cc + 7 share a coordinate: one run of the table
+              const bool on_row = 8 * cc < D / 4;
+              const float2* tb = s_cs + (on_row ? pc.x : pc.y) * (D / 4) + (on_row ? 8 * cc : 8 * cc - D / 4);
+              rotate([&](int pr, int, int, float& cs, float& sn) {
+                const float2 v = tb[pr];
+                cs = v.x;
+                sn = v.y;
+              });
+            } else {
+              rotate([&](int, int ci, int f, float& cs, float& sn) {
+                const float2 v = s_cs[ci * (D / 4) + f];
+                cs = v.x;
+                sn = v.y;
+              });
+            }
           } else {
-            rotate([&](int ci, int f, float& cs, float& sn) {
+            rotate([&](int, int ci, int f, float& cs, float& sn) {
               const float coord = float(ci);
               const float2 rv = s_rev[f];
               const float tt = coord * rv.x;
@@ -768,6 +834,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
           *p1 = __builtin_bit_cast(u32x4_t, y1);
         }
       }
+      };
+      if (qpre.rope_mode == 0)
+        run(std::true_type{});
+      else
+        run(std::false_type{});
     };
 
     // Sum of p over the whole row b (both lane halves).

@@ -319,9 +319,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
   __shared__ float s_qw[D];
   __shared__ float s_kw[C::KF ? D : 1];
   __shared__ float2 s_rev[kMaxQFreqs];
-  __shared__ float2 s_cs[C::QT ? kRopeCoords * (D / 4) : 1];
+  // Rotary table rows (one per coordinate) are D/4 + 2 entries apart, so
+  // rows of different coordinates start 4 banks apart: lanes reading the
+  // same frequency of different coordinates do not share banks.
+  constexpr int kCsRow = D / 4 + 2;
+  __shared__ float2 s_cs[C::QT ? kRopeCoords * kCsRow : 1];
   static_assert((C::LDS_BYTES + (C::KF ? 2 : 1) * D * 4 + kMaxQFreqs * 8 +
-                 (C::QT ? kRopeCoords * (D / 4) * 8 : 0)) * C::WG_PER_CU <= 160 * 1024,
+                 (C::QT ? kRopeCoords * kCsRow * 8 : 0)) * C::WG_PER_CU <= 160 * 1024,
                 "LDS budget with the pre-pass tables");
   const bool q_pending = qpre.pos != nullptr || qpre.weight != nullptr;
   if (q_pending || C::KF) {
@@ -347,7 +351,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
         const float2 rv = s_rev[e % (D / 4)];
         const float t = coord * rv.x;
         const float frac = (t - rintf(t)) + (fmaf(coord, rv.x, -t) + coord * rv.y);
-        s_cs[e] = make_float2(__builtin_amdgcn_cosf(frac), __builtin_amdgcn_sinf(frac));
+        s_cs[(e / (D / 4)) * kCsRow + e % (D / 4)] =
+            make_float2(__builtin_amdgcn_cosf(frac), __builtin_amdgcn_sinf(frac));
       }
       __syncthreads();
     }
@@ -570,7 +575,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
           // the wave has both coordinates below kRopeCoords.
           auto cossin_table = [&](int m, float& cs, float& sn) {
             const int coord = m < QUART ? pc.x : pc.y;
-            const float2 v = s_cs[coord * QUART + (m < QUART ? m : m - QUART)];
+            const float2 v = s_cs[coord * kCsRow + (m < QUART ? m : m - QUART)];
             cs = v.x;
             sn = v.y;
           };
@@ -630,7 +635,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
                   const bool first = st < kFirstRegs;
                   const int m0 = 16 * st + 8 * half - (first ? 0 : HALF);
                   const bool on_row = m0 < QUART;
-                  const float2* tb = s_cs + (on_row ? pc.x : pc.y) * QUART + (on_row ? m0 : m0 - QUART);
+                  const float2* tb = s_cs + (on_row ? pc.x : pc.y) * kCsRow + (on_row ? m0 : m0 - QUART);
 #pragma unroll
                   for (int i = 0; i < 8; ++i) {
                     const float partner = x[(st + HALF / 16) % KS][i];
@@ -644,7 +649,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
               for (int st = 0; st < KS; ++st) {
                 const int j0 = 8 * st + 4 * half;
                 const bool on_row = j0 < QUART;
-                const float2* tb = s_cs + (on_row ? pc.x : pc.y) * QUART + (on_row ? j0 : j0 - QUART);
+                const float2* tb = s_cs + (on_row ? pc.x : pc.y) * kCsRow + (on_row ? j0 : j0 - QUART);
 #pragma unroll
                 for (int i = 0; i < 8; i += 2) {
                   const float2 v = tb[i / 2];
@@ -796,22 +801,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
             }
           };
           if (__all(unsigned(pc.x) < unsigned(kRopeCoords) && unsigned(pc.y) < unsigned(kRopeCoords))) {
-            if constexpr ((D / 4) % 8 == 0) {
-              // pairs 8 cc .. 8 cc + 7 share a coordinate: one run of the table
-              const bool on_row = 8 * cc < D / 4;
-              const float2* tb = s_cs + (on_row ? pc.x : pc.y) * (D / 4) + (on_row ? 8 * cc : 8 * cc - D / 4);
-              rotate([&](int pr, int, int, float& cs, float& sn) {
-                const float2 v = tb[pr];
-                cs = v.x;
-                sn = v.y;
-              });
-            } else {
-              rotate([&](int, int ci, int f, float& cs, float& sn) {
-                const float2 v = s_cs[ci * (D / 4) + f];
-                cs = v.x;
-                sn = v.y;
-              });
-            }
+            // One 8-byte read per pair.  Reading a lane's eight pairs as one
+            // 64-byte run was slower (ragged batch 908 against 692 us): the
+            // lanes of a key then read runs 64 bytes apart, on the same banks.
+            rotate([&](int, int ci, int f, float& cs, float& sn) {
+              const float2 v = s_cs[ci * kCsRow + f];
+              cs = v.x;
+              sn = v.y;
+            });
           } else {
             rotate([&](int, int ci, int f, float& cs, float& sn) {
               const float coord = float(ci);

@@ -83,6 +83,23 @@ def test_fused_q_large_positions_and_theta():
     assert_attn_close(got, _want(wl, x), "bf16", "fused q 96x96")
 
 
+@pytest.mark.parametrize("D", [64, 80, 128])
+@pytest.mark.parametrize("rope_mode", ["neox", "complex"])
+def test_fused_q_positions_outside_the_table(D, rope_mode):
+    """Negative coordinates and coordinates of 64 and more next to small
+    ones: waves with any of them evaluate the angles directly, the others read
+    the workgroup's table."""
+    wl = W.custom([(10, 13), (7, 9), (3, 40)], H=2, D=D, dtype="bf16", seed=97, use_norm=True)
+    x = W.generate(wl)
+    rng = np.random.default_rng(97)
+    pos = x.pos.astype(np.int64)
+    pos[:130] += rng.integers(-200, 200, size=(130, 2))
+    pos[193:] = rng.integers(60, 70, size=(wl.total_tokens - 193, 2))
+    x.pos = pos.astype(np.int32)
+    got, _ = _fused(wl, x, rope_mode)
+    assert_attn_close(got, _want(wl, x, rope_mode), "bf16", f"fused q positions D={D}")
+
+
 @pytest.mark.parametrize("n", [2, 3])
 def test_fused_q_workload(n):
     """4 x (32 x 32) at D = 80, and the 24-image ragged batch at D = 128 with

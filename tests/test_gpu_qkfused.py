@@ -88,7 +88,7 @@ def test_fused_qk_norm_only(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 80, 128])
 def test_fused_qk_causal(dtype, D):
     wl = W.custom(GRIDS, H=2, D=D, dtype=dtype, seed=127, use_norm=True)
     x = W.generate(wl)
@@ -103,6 +103,23 @@ def test_fused_qk_large_positions():
     x = W.generate(wl)
     got, _ = _fused(wl, x)
     assert_attn_close(got, _want(wl, x), "bf16", "fused qk 96x96")
+
+
+@pytest.mark.parametrize("D", [64, 80, 128])
+@pytest.mark.parametrize("rope_mode", ["neox", "complex"])
+def test_fused_qk_positions_outside_the_table(D, rope_mode):
+    """Negative coordinates and coordinates of 64 and more: the rows and keys
+    whose wave has any of them take the directly evaluated angles, the others
+    the workgroup's table, in the same launch."""
+    wl = W.custom([(10, 13), (7, 9), (3, 40)], H=2, D=D, dtype="bf16", seed=133, use_norm=True)
+    x = W.generate(wl)
+    rng = np.random.default_rng(133)
+    pos = x.pos.astype(np.int64)
+    pos[:130] += rng.integers(-200, 200, size=(130, 2))      # first segment: anywhere
+    pos[193:] = rng.integers(60, 70, size=(wl.total_tokens - 193, 2))  # straddling 64
+    x.pos = pos.astype(np.int32)
+    got, _ = _fused(wl, x, rope_mode)
+    assert_attn_close(got, _want(wl, x, rope_mode), "bf16", f"fused qk positions D={D}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

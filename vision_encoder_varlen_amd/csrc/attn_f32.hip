@@ -1,6 +1,6 @@
 // Varlen (block-diagonal) attention in fp32 throughout, non-causal or causal.
 //
-// Same operation as attn_bf16.hip (vLLM page
+// Same operation as the bf16 kernel of attn_bf16_kernel.h (vLLM page
 // vllm.models.dots3_note.nvidia.vision_attention, VisionAttentionV2.forward),
 // for fp32 tensors where an exact-precision result is wanted.  No MFMA and no
 // down-conversion: products and sums are fp32 FMAs and the softmax uses the

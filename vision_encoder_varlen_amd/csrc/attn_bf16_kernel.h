@@ -84,6 +84,9 @@ constexpr int kRsrcWord3 = 0x00020000;    // gfx9-family buffer descriptor word 
 // Rotary coordinates below this come from a per-workgroup table of cos and
 // sin (fused q/k kernels); larger ones are evaluated directly.
 constexpr int kRopeCoords = 64;
+// Output rows staged through LDS before the global stores (see the kernel's
+// finalize step).
+constexpr bool kStageOut = true;
 // Byte offset for copy lanes that fill padding: past any segment's num_records
 // (segments are limited to kMaxSegmentBytes) even after adding the tile offset.
 constexpr unsigned kPadOffset = 0x40000000u;
@@ -295,22 +298,28 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
       cp_lds[j] = unsigned((C::KREG + C::VREG) * 16 + pi * 256);
     }
   }
-  if constexpr (kSumByMfma) {
-    // V row padding of every ring stage: unit DU starts with bf16 1.0 (dim D),
-    // the rest are zero.  No copy writes these units (cp_skip), and the first
-    // tile's barrier orders these stores before any read.
-    static_assert(C::VSTR > C::DU && kOnesLane % 8 == 0, "dim D must open a padding unit");
-    constexpr int kPadUnits = C::VSTR - C::DU;
-    for (int i = tid; i < STAGES * BN * kPadUnits; i += C::THREADS) {
-      const int stage = i / (BN * kPadUnits);
-      const int r = (i / kPadUnits) % BN;
-      const int pu = i % kPadUnits;
-      u32x4_t val = u32x4_t{0u, 0u, 0u, 0u};
-      if (pu == 0) val.x = 0x3f80u;  // dims D, D+1 = (1.0, 0) in the low dword
-      *reinterpret_cast<u32x4_t*>(smem + (stage * C::STAGE_UNITS + C::KREG + r * C::VSTR + C::DU + pu) * 8) =
-          val;
+  // V row padding of every ring stage: unit DU starts with bf16 1.0 (dim D),
+  // the rest are zero.  No copy writes these units (cp_skip), and the first
+  // tile's barrier orders these stores before any read.  Written here, and
+  // again at the start of every later unit when the previous unit's output
+  // was staged through the ring.
+  auto write_ones = [&]() __attribute__((always_inline)) {
+    if constexpr (kSumByMfma) {
+      static_assert(C::VSTR > C::DU && kOnesLane % 8 == 0, "dim D must open a padding unit");
+      constexpr int kPadUnits = C::VSTR - C::DU;
+      for (int i = tid; i < STAGES * BN * kPadUnits; i += C::THREADS) {
+        const int stage = i / (BN * kPadUnits);
+        const int r = (i / kPadUnits) % BN;
+        const int pu = i % kPadUnits;
+        u32x4_t val = u32x4_t{0u, 0u, 0u, 0u};
+        if (pu == 0) val.x = 0x3f80u;  // dims D, D+1 = (1.0, 0) in the low dword
+        *reinterpret_cast<u32x4_t*>(smem + (stage * C::STAGE_UNITS + C::KREG + r * C::VSTR + C::DU + pu) *
+                                               8) = val;
+      }
     }
-  }
+  };
+  write_ones();
+  bool ring_staged = false;  // the previous unit's output went through the ring
 
   // Q-side pre-pass (when asked for): each unit's Q fragments are normalised
   // and rotated in registers right after they are loaded.  The tables hold
@@ -996,6 +1005,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     // older Q loads, and the first tiles' copies overlap them.
     auto start_pass = [&]() {
       __syncthreads();
+      if constexpr (kStageOut && kSumByMfma) {
+        if (ring_staged) {  // every wave has read its staged rows back (barrier above)
+          write_ones();
+          ring_staged = false;
+        }
+      }
 #pragma unroll
       for (int t = 0; t < STAGES - 1; ++t)
         if (t < ntiles) issue_tile(t);
@@ -1059,6 +1074,55 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
     }
 
     // Finalize: O^T register r of block d holds dim 32d + 8(r>>2) + 4half + (r&3).
+    // With kStageOut the normalised rows go through LDS first (the ring is
+    // free once every wave is past its last tile) and leave as whole 16-byte
+    // pieces, lane-consecutive along each row; written straight from the
+    // accumulators, each store instruction would put 16 bytes into each of 32
+    // rows.
+    if constexpr (kStageOut) {
+      constexpr int kORow = D * 2 + 16;    // staged row stride, bytes
+      constexpr int kCPR = D / 8;          // 16-byte pieces per row
+      static_assert(C::WAVES * 32 * QB * kORow <= C::LDS_BYTES, "output staging fits the ring");
+      static_assert((32 * QB * kCPR) % 64 == 0, "whole store rounds per wave");
+      __syncthreads();  // every wave is past its last tile: the ring is free
+      ring_staged = true;
+      char* const ost = reinterpret_cast<char*>(smem) + wave * (32 * QB * kORow);
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        const int row = row0 + 32 * b + l32;
+        const float l_tot = row_total(b);
+        // Log-sum-exp of the row's scores, natural log: p = 2^(x - m_ref)
+        // with x = scale * log2(e) * score, so sum_b e^(scale*score) = 2^m_ref * l.
+        if (lse != nullptr && row < len)
+          lse[size_t(start + row) * H + h] = (m_ref[b] + log2f(l_tot)) * kLn2;
+        const float inv = 1.f / l_tot;  // rows past the segment are staged, never stored
+        char* const orow = ost + (32 * b + l32) * kORow;
+#pragma unroll
+        for (int d = 0; d < C::DB; ++d) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = d * 32 + 8 * g + 4 * half;
+            if (d0 < D) {
+              __bf16 w[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[b][d][4 * g + e] * inv);
+              *reinterpret_cast<u32x2_t*>(orow + d0 * 2) = __builtin_bit_cast(u32x2_t, w);
+            }
+          }
+        }
+      }
+      // A wave reads back only what it wrote, and a wave's LDS accesses are
+      // carried out in order.
+#pragma unroll
+      for (int it = 0; it < 32 * QB * kCPR / 64; ++it) {
+        const int c = it * 64 + lane;
+        const int r = c / kCPR, col = c - r * kCPR;
+        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ost + r * kORow + col * 16);
+        if (row0 + r < len)
+          *reinterpret_cast<u32x4_t*>(out + size_t(start + row0 + r) * ts.o + size_t(h) * D + col * 8) =
+              val;
+      }
+    } else {
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
       const int row = row0 + 32 * b + l32;
@@ -1084,6 +1148,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_bf16_kernel(
           }
         }
       }
+    }
     }
   }
 }

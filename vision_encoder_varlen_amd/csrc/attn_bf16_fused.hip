@@ -4,7 +4,9 @@
 // applied to q's rows as they are loaded (PRE 1, q only) and, with fuse_k,
 // to every K tile in LDS as well (PRE 2), as the FA4 route on the tokenspeed
 // page (MultimodalEncoderAttention.forward) fuses the rotary into the QKV
-// split.
+// split.  Every call that asks for any part of the pre-pass is launched
+// from here; the plain kernels (PRE 0) still hold a direct query transform
+// behind a runtime test, which these calls never reach.
 #include "attn_bf16_kernel.h"
 
 namespace vit {

@@ -270,6 +270,11 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path runs on a "
               "single GPU).", file=sys.stderr)
         sys.exit(2)
+    # Step forms that exclude each other, refused before any GPU work.
+    if args.fuse_q and args.fuse_qk:
+        sys.exit("bench: --fuse-q and --fuse-qk are two forms of the step; pick one")
+    if args.dense_batch and (args.fuse_q or args.fuse_qk):
+        sys.exit("bench: --fuse-q / --fuse-qk time the work-list step; drop --dense-batch")
 
     import torch
     from vision_encoder_varlen_amd import _lib, ops

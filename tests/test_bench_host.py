@@ -24,6 +24,16 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert r.stdout == ""
 
 
+@pytest.mark.parametrize("flags", [["--fuse-q", "--fuse-qk"], ["--fuse-qk", "--dense-batch"],
+                                   ["--fuse-q", "--dense-batch"]])
+def test_exclusive_step_forms_are_refused_before_any_gpu_work(flags):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *flags],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "bench:" in r.stderr
+    assert r.stdout == ""
+
+
 @pytest.mark.parametrize("cfg,bound", [(2, "mfma"), (3, "mfma"), (4, "mfma"), (5, "hbm")])
 def test_roofline_bound_per_workload(cfg, bound):
     wl = W.config(cfg)
